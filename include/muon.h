@@ -1,0 +1,177 @@
+/*
+ * muon.h -- C ABI of the MI355X (gfx950) Muon optimizer step.
+ *
+ * The operation (per hidden weight matrix W with gradient G and momentum
+ * buffer M), as the pages describe it:
+ *   - Guide page "NanoGPT Speedrun: The Ultimate Guide to Pushing LLM Training
+ *     Efficiency to Its Limits", section "Optimizer and Training Strategy
+ *     Tuning": Muon is applied to hidden-layer matrix weights only; the update
+ *     is orthogonalised after a Nesterov momentum step.
+ *   - Overview page "The NanoGPT speedrun", paragraph "Six records account for
+ *     most of the speedup" (record #3): the momentum update is replaced by its
+ *     nearest semi-orthogonal matrix through five Newton-Schulz steps.
+ *
+ * What muon_step computes, per matrix (rows x cols, row-major):
+ *   M <- fl32(mu*M + G)                       momentum, fp32 buffer, in place
+ *   U  = G + mu*M   (nesterov != 0)  or  U = M
+ *   X  = U, or U^T when rows > cols           short side first (m <= n)
+ *   X <- X / (||X||_F + 1e-7)
+ *   T times:  A = X X^T;  B = b*A + c*A*A;  X <- a*X + B*X
+ *   W <- W - lr * s * O,  O = X (or X^T back in W's orientation)
+ * s is the descriptor's `scale` (<= 0 means 1).  The polynomial, the
+ * normalisation and s are readings of the pages, which name the iteration but
+ * not its coefficients; a, b, c and T are arguments.
+ *
+ * Precision.  MUON_PATH_BF16: the three products take bf16 operands (rounded
+ * to nearest even) and accumulate in fp32; A and B are stored bf16; the a*X
+ * term reads an fp32 copy of X for the first `x_master_iters` iterations
+ * (default 3) and the bf16 copy afterwards.  Matrices whose short side is
+ * below 64 take the fp32 arithmetic even on this path: their A*A and B*X
+ * contractions are too short for bf16 rounding errors to average out.
+ * MUON_PATH_F32: everything fp32.
+ *
+ * Ownership.  The caller owns every device buffer: weights, gradients,
+ * momentum buffers and the workspace.  The library never allocates device
+ * memory.  A plan (host object) holds the layout and its device tables, which
+ * live inside the caller's workspace; the workspace must stay untouched and
+ * alive for the plan's lifetime.  A plan is not re-entrant: calls on one plan
+ * must be ordered (one stream, or synchronised streams).  Different plans
+ * with different workspaces may run concurrently.
+ *
+ * Streams.  `hip_stream` is a hipStream_t passed as void* (NULL = the null
+ * stream).  muon_step only enqueues work (it never waits for the device
+ * unless a pointer change finds all 8 device copies of the matrix table
+ * still in flight); inputs must stay alive until the stream has passed the
+ * step.
+ *
+ * Errors.  Every int-returning function returns MUON_OK (0) or a negative
+ * MUON_E_* code and then sets a thread-local message readable with
+ * muon_last_error().  No C++ exception crosses this ABI.  Gradient values are
+ * not inspected: NaN/Inf in G propagate into M, X and W.
+ */
+#ifndef MUON_MI355X_H
+#define MUON_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MUON_OK 0
+#define MUON_E_INVAL (-1)       /* bad argument: null pointer, size, T, non-finite scalar ... */
+#define MUON_E_UNSUPPORTED (-2) /* dtype or leading dimension not supported */
+#define MUON_E_MISMATCH (-3)    /* step descriptors do not match the plan */
+#define MUON_E_WORKSPACE (-4)   /* workspace too small or not 256-byte aligned */
+#define MUON_E_HIP (-5)         /* a HIP runtime call failed (message has its text) */
+
+#define MUON_DTYPE_F32 0
+#define MUON_DTYPE_BF16 1
+
+#define MUON_PATH_BF16 0
+#define MUON_PATH_F32 1
+
+/* One hidden matrix.  All pointers are device pointers.  Row-major storage;
+ * ld_w and ld_g are leading dimensions in elements and must equal cols (0 is
+ * read as cols).  grad: MUON_DTYPE_BF16 or MUON_DTYPE_F32.  weight:
+ * MUON_DTYPE_F32 or MUON_DTYPE_BF16.  momentum: always fp32, rows x cols.
+ * weight must not alias grad or momentum. */
+typedef struct muon_matrix_desc {
+  void* weight;
+  const void* grad;
+  float* momentum;
+  int64_t rows;
+  int64_t cols;
+  int64_t ld_w;
+  int64_t ld_g;
+  int32_t w_dtype;
+  int32_t g_dtype;
+  float scale;      /* per-matrix factor s of the weight step; <= 0 means 1 */
+  int32_t reserved; /* must be 0 */
+} muon_matrix_desc;
+
+/* Plan options.  NULL means: MUON_PATH_BF16, x_master_iters 3, no zeroing,
+ * max_T 64. */
+typedef struct muon_options {
+  int32_t path;           /* MUON_PATH_BF16 or MUON_PATH_F32 */
+  int32_t x_master_iters; /* bf16 path: iterations 1..k read an fp32 copy of X in
+                             a*X; < 0 selects the default 3; ignored on f32 */
+  int32_t zero_momentum;  /* != 0: muon_init zeroes every momentum buffer */
+  int32_t max_T;          /* largest T muon_step accepts; <= 0 selects 64 */
+} muon_options;
+
+typedef struct muon_plan muon_plan;
+
+/* Library version string, e.g. "muon-mi355x 1.0.0 (gfx950)".  Never NULL. */
+const char* muon_version(void);
+
+/* Bytes of device workspace muon_init needs for these matrices and options;
+ * 0 on invalid arguments (see muon_last_error).  Host-only: no HIP call. */
+size_t muon_workspace_size(const muon_matrix_desc* descs, int n, const muon_options* opts);
+
+/* Validate the n descriptors, plan the launches and lay out the workspace
+ * (device memory of ws_bytes >= muon_workspace_size(...), 256-byte aligned).
+ * Uploads the plan's tables (and zeroes the momentum buffers when requested)
+ * on hip_stream and waits for that stream before returning.  On success
+ * *out_plan owns the host state. */
+int muon_init(const muon_matrix_desc* descs, int n, const muon_options* opts,
+              void* workspace, size_t ws_bytes, void* hip_stream, muon_plan** out_plan);
+
+/* Enqueue one Muon step over every matrix of the plan on hip_stream:
+ * 1 momentum/norm launch, then 3 launches per Newton-Schulz iteration (all
+ * matrices of one precision grouped in each launch: 6 per iteration when the
+ * plan mixes bf16 and fp32 matrices); T == 0 enqueues one weight-step launch
+ * instead (W <- W - lr*s*X0).  descs == NULL reuses the pointers the plan
+ * holds; otherwise n must equal the plan's count and shapes, dtypes and
+ * scales must match (pointers may differ).  Requirements: 0 <= T <= max_T,
+ * 0 <= momentum <= 1, a, b, c, lr finite. */
+int muon_step(muon_plan* plan, const muon_matrix_desc* descs, int n, float a, float b, float c,
+              int T, float momentum, int nesterov, float lr, void* hip_stream);
+
+/* Free the plan's host state.  The workspace stays the caller's. */
+int muon_destroy(muon_plan* plan);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* muon_last_error(void);
+
+/* ---- introspection and measurement ---------------------------------------- */
+
+/* Launch kinds, in the order they run within a step. */
+#define MUON_KIND_MOMENTUM 0 /* momentum + Nesterov + Frobenius partial sums, writes X0 */
+#define MUON_KIND_GRAM 1     /* A = X X^T (upper tiles, mirrored) */
+#define MUON_KIND_POLY 2     /* B = b A + c A A (upper tiles, mirrored) */
+#define MUON_KIND_UPDATE 3   /* X <- a X + B X; on the last iteration W <- W - lr s O */
+#define MUON_KIND_APPLY 4    /* T == 0 only: W <- W - lr s X0 */
+#define MUON_KIND_COUNT 5
+
+/* Host-only description of the plan these descriptors would get.  Returns
+ * MUON_OK and fills the fields, or an error code.  `tiles` (optional) gets
+ * the launch-ordered tile list of one kind as (matrix, tile_row, tile_col)
+ * int32 triples, at most tile_cap triples; *n_tiles gets the full count. */
+typedef struct muon_plan_info {
+  int64_t workspace_bytes;
+  int32_t n_matrices;
+  int32_t tile;              /* tile edge of the Newton-Schulz products */
+  int32_t blocks[MUON_KIND_COUNT]; /* grid size of each launch kind */
+  int32_t x_master_iters;
+  int32_t path;
+  int32_t n_f32_matrices;    /* matrices whose products run in fp32 (see below) */
+} muon_plan_info;
+
+int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts,
+                  muon_plan_info* info, int kind, int32_t* tiles, int tile_cap, int32_t* n_tiles);
+
+/* Per-launch timing with HIP events recorded around every launch of
+ * muon_step (enable != 0 turns it on; it adds event records to the stream).
+ * muon_profile_read waits for the recorded events, adds their durations per
+ * kind into ms[MUON_KIND_COUNT] and launches[MUON_KIND_COUNT] (totals since
+ * the last read), and resets the totals. */
+int muon_profile_enable(muon_plan* plan, int enable);
+int muon_profile_read(muon_plan* plan, double* ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_MI355X_H */

@@ -1,0 +1,659 @@
+// Host side of the Muon C ABI: validation, planning, workspace layout,
+// launch sequence and per-launch timing.  See include/muon.h for the
+// contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/muon.h"
+#include "muon_internal.h"
+
+namespace muon {
+hipError_t launch_momentum(const MomArgs& args, int blocks, hipStream_t stream);
+hipError_t launch_apply(const ApplyArgs& args, int blocks, hipStream_t stream);
+hipError_t launch_stage(int stage, bool f32, const StageArgs& args, int blocks, hipStream_t stream);
+}  // namespace muon
+
+using namespace muon;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MUON_E_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+constexpr int kSlots = 8;           // device copies of the matrix table (pointer updates)
+constexpr size_t kAlign = 256;
+constexpr int kMaxMatrices = 65000; // tile tables index matrices with 16 bits
+constexpr int64_t kMaxDim = 1 << 20;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+struct Options {
+  int path = MUON_PATH_BF16;
+  int kmaster = 3;
+  int zero = 0;
+  int maxT = 64;
+};
+
+int read_options(const muon_options* o, Options* out) {
+  Options r;
+  if (o) {
+    if (o->path != MUON_PATH_BF16 && o->path != MUON_PATH_F32)
+      return fail(MUON_E_UNSUPPORTED, "options.path %d is not MUON_PATH_BF16 or MUON_PATH_F32", o->path);
+    r.path = o->path;
+    r.kmaster = o->x_master_iters < 0 ? 3 : o->x_master_iters;
+    r.zero = o->zero_momentum;
+    r.maxT = o->max_T <= 0 ? 64 : o->max_T;
+    if (r.maxT > 4096) return fail(MUON_E_INVAL, "options.max_T %d exceeds 4096", r.maxT);
+    if (r.kmaster > 4096) return fail(MUON_E_INVAL, "options.x_master_iters %d exceeds 4096", r.kmaster);
+  }
+  if (r.path == MUON_PATH_F32) r.kmaster = 0;
+  *out = r;
+  return MUON_OK;
+}
+
+// Shape/dtype check of one descriptor.  `need_ptrs`: pointers must be set.
+int check_desc(const muon_matrix_desc& d, int idx, bool need_ptrs) {
+  if (d.rows <= 0 || d.cols <= 0)
+    return fail(MUON_E_INVAL, "matrix %d: rows=%lld cols=%lld must be positive", idx, (long long)d.rows,
+                (long long)d.cols);
+  if (d.rows > kMaxDim || d.cols > kMaxDim)
+    return fail(MUON_E_INVAL, "matrix %d: %lld x %lld exceeds the %lld limit per side", idx, (long long)d.rows,
+                (long long)d.cols, (long long)kMaxDim);
+  if (d.ld_w != 0 && d.ld_w != d.cols)
+    return fail(MUON_E_UNSUPPORTED, "matrix %d: ld_w=%lld must equal cols=%lld", idx, (long long)d.ld_w,
+                (long long)d.cols);
+  if (d.ld_g != 0 && d.ld_g != d.cols)
+    return fail(MUON_E_UNSUPPORTED, "matrix %d: ld_g=%lld must equal cols=%lld", idx, (long long)d.ld_g,
+                (long long)d.cols);
+  if (d.g_dtype != MUON_DTYPE_BF16 && d.g_dtype != MUON_DTYPE_F32)
+    return fail(MUON_E_UNSUPPORTED, "matrix %d: g_dtype %d unsupported", idx, d.g_dtype);
+  if (d.w_dtype != MUON_DTYPE_BF16 && d.w_dtype != MUON_DTYPE_F32)
+    return fail(MUON_E_UNSUPPORTED, "matrix %d: w_dtype %d unsupported", idx, d.w_dtype);
+  if (d.reserved != 0) return fail(MUON_E_INVAL, "matrix %d: reserved field must be 0", idx);
+  if (!std::isfinite(d.scale)) return fail(MUON_E_INVAL, "matrix %d: scale is not finite", idx);
+  if (need_ptrs) {
+    if (!d.weight || !d.grad || !d.momentum) return fail(MUON_E_INVAL, "matrix %d: null device pointer", idx);
+    if (d.weight == d.grad || d.weight == (void*)d.momentum || d.grad == (const void*)d.momentum)
+      return fail(MUON_E_INVAL, "matrix %d: weight, grad and momentum must be distinct buffers", idx);
+    const size_t wal = d.w_dtype == MUON_DTYPE_F32 ? 4 : 2, gal = d.g_dtype == MUON_DTYPE_F32 ? 4 : 2;
+    if ((uintptr_t)d.weight % wal || (uintptr_t)d.grad % gal || (uintptr_t)d.momentum % 4)
+      return fail(MUON_E_INVAL, "matrix %d: pointer not aligned to its element size", idx);
+  }
+  return MUON_OK;
+}
+
+struct Layout {
+  // per matrix byte offsets into the workspace
+  struct M {
+    size_t x32, xo0, xo1, a, b, part, sc;
+  };
+  std::vector<M> m;
+  size_t slots = 0, slot_bytes = 0;
+  size_t mom_tiles = 0;
+  size_t ns_tiles[2][3] = {};
+  size_t total = 0;
+};
+
+struct Geometry {
+  int rows, cols, m, n, mp, np, tr, nparts, mom_n, f32;
+};
+
+Geometry geometry(const muon_matrix_desc& d, int path) {
+  Geometry g;
+  g.rows = (int)d.rows;
+  g.cols = (int)d.cols;
+  g.tr = d.rows > d.cols;
+  g.m = (int)std::min(d.rows, d.cols);
+  g.n = (int)std::max(d.rows, d.cols);
+  g.mp = (int)round_up(g.m, kTile);
+  g.np = (int)round_up(g.n, kTile);
+  g.mom_n = g.np / kMomTile;
+  g.nparts = (g.mp / kMomTile) * g.mom_n;
+  g.f32 = path == MUON_PATH_F32 || g.m < kMinBf16Side;
+  return g;
+}
+
+// Tile lists: the momentum list covers every matrix; the product lists are
+// split by operand precision (index 0: bf16 matrices, 1: fp32 matrices),
+// since each launch runs one precision.
+enum { kGram = 0, kPoly = 1, kUpd = 2 };
+struct Tables {
+  std::vector<Tile> mom;
+  std::vector<Tile> ns[2][3];
+};
+
+// Tiles of one kind, ordered for the MI355X dispatcher, which places block b
+// on XCD b % 8.  All tiles are listed matrix by matrix (most expensive
+// matrices first), the list is cut into 8 contiguous runs of equal total cost,
+// and run x is laid on blocks x, x+8, x+16, ...  Each XCD therefore works on
+// few matrices at a time (they stay in its L2) and the XCDs get equal work;
+// shorter runs are padded with null tiles that exit at once.
+std::vector<Tile> xcd_order(const std::vector<std::vector<Tile>>& per_mat, const std::vector<double>& tile_cost) {
+  const int nm = (int)per_mat.size();
+  std::vector<int> order(nm);
+  for (int i = 0; i < nm; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return tile_cost[x] > tile_cost[y]; });
+  double total = 0.0;
+  for (int i = 0; i < nm; ++i) total += tile_cost[i] * per_mat[i].size();
+  if (total <= 0.0) return {};
+  std::vector<std::vector<Tile>> runs(kXcds);
+  double acc = 0.0;
+  for (int i : order) {
+    for (const Tile& t : per_mat[i]) {
+      // the run whose cost share contains the midpoint of this tile
+      int x = (int)((acc + 0.5 * tile_cost[i]) * kXcds / total);
+      x = std::min(std::max(x, 0), kXcds - 1);
+      runs[x].push_back(t);
+      acc += tile_cost[i];
+    }
+  }
+  size_t longest = 0;
+  for (int x = 0; x < kXcds; ++x) longest = std::max(longest, runs[x].size());
+  std::vector<Tile> out(longest * kXcds, Tile{kNullMat, 0, 0, 0});
+  for (int x = 0; x < kXcds; ++x)
+    for (size_t q = 0; q < runs[x].size(); ++q) out[q * kXcds + x] = runs[x][q];
+  while (!out.empty() && out.back().mat == kNullMat) out.pop_back();
+  return out;
+}
+
+Tables build_tables(const std::vector<Geometry>& geo) {
+  Tables t;
+  const int nm = (int)geo.size();
+  for (int prec = 0; prec < 2; ++prec) {
+    std::vector<std::vector<Tile>> sym(nm), upd(nm);
+    std::vector<double> gram_cost(nm), poly_cost(nm), upd_cost(nm);
+    for (int i = 0; i < nm; ++i) {
+      const Geometry& g = geo[i];
+      if (g.f32 != prec) continue;
+      const int tm = g.mp / kTile, tn = g.np / kTile;
+      for (int a = 0; a < tm; ++a)
+        for (int b = a; b < tm; ++b) sym[i].push_back(Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0});
+      for (int a = 0; a < tm; ++a)
+        for (int b = 0; b < tn; ++b) upd[i].push_back(Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0});
+      gram_cost[i] = (double)g.np;  // K of each product tile
+      poly_cost[i] = (double)g.mp;
+      upd_cost[i] = (double)g.mp;
+    }
+    t.ns[prec][kGram] = xcd_order(sym, gram_cost);
+    t.ns[prec][kPoly] = xcd_order(sym, poly_cost);
+    t.ns[prec][kUpd] = xcd_order(upd, upd_cost);
+  }
+  for (int i = 0; i < nm; ++i) {
+    const Geometry& g = geo[i];
+    for (int a = 0; a < g.mp / kMomTile; ++a)
+      for (int b = 0; b < g.np / kMomTile; ++b) t.mom.push_back(Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0});
+  }
+  return t;
+}
+
+size_t layout(const std::vector<Geometry>& geo, const Options& o, const Tables& t, Layout* L) {
+  const int nm = (int)geo.size();
+  size_t off = 0;
+  L->slot_bytes = align_up(sizeof(DevMat) * nm, kAlign);
+  L->slots = off;
+  off += L->slot_bytes * kSlots;
+  L->mom_tiles = off;
+  off = align_up(off + sizeof(Tile) * t.mom.size(), kAlign);
+  for (int prec = 0; prec < 2; ++prec)
+    for (int k = 0; k < 3; ++k) {
+      L->ns_tiles[prec][k] = off;
+      off = align_up(off + sizeof(Tile) * t.ns[prec][k].size(), kAlign);
+    }
+  L->m.resize(nm);
+  for (int i = 0; i < nm; ++i) {
+    const Geometry& g = geo[i];
+    const size_t es = g.f32 ? 4 : 2;
+    const size_t xe = (size_t)g.mp * g.np, ae = (size_t)g.mp * g.mp;
+    Layout::M& m = L->m[i];
+    m.x32 = (size_t)-1;
+    if (!g.f32 && o.kmaster > 0) {
+      m.x32 = off;
+      off = align_up(off + xe * 4, kAlign);
+    }
+    m.xo0 = off;
+    off = align_up(off + xe * es, kAlign);
+    m.xo1 = off;
+    off = align_up(off + xe * es, kAlign);
+    m.a = off;
+    off = align_up(off + ae * es, kAlign);
+    m.b = off;
+    off = align_up(off + ae * es, kAlign);
+    m.part = off;
+    off = align_up(off + sizeof(float) * g.nparts, kAlign);
+    m.sc = off;
+    off = align_up(off + 4 * sizeof(float), kAlign);
+  }
+  L->total = off;
+  return off;
+}
+
+int validate_all(const muon_matrix_desc* d, int n, bool need_ptrs) {
+  if (!d) return fail(MUON_E_INVAL, "descriptor array is NULL");
+  if (n <= 0 || n > kMaxMatrices) return fail(MUON_E_INVAL, "matrix count %d outside [1, %d]", n, kMaxMatrices);
+  for (int i = 0; i < n; ++i) {
+    int rc = check_desc(d[i], i, need_ptrs);
+    if (rc) return rc;
+  }
+  return MUON_OK;
+}
+
+}  // namespace
+
+struct muon_plan {
+  int n = 0;
+  Options opt;
+  std::vector<Geometry> geo;
+  std::vector<muon_matrix_desc> desc;  // shapes, dtypes, scales and current pointers
+  Tables tab;
+  Layout lay;
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  std::vector<DevMat> hmat;            // host image of the current table
+  DevMat* host_slots[kSlots] = {};     // pinned staging, one per device slot
+  hipEvent_t slot_ev[kSlots] = {};
+  bool slot_used[kSlots] = {};
+  int slot = 0;
+  hipEvent_t last_ev = nullptr;        // recorded after the last enqueued work
+  bool last_valid = false;
+  // profiling
+  bool prof = false;
+  std::vector<hipEvent_t> pev;         // pairs: start, stop
+  std::vector<int> pkind;              // kind of each pair
+  size_t pused = 0;
+  double pms[MUON_KIND_COUNT] = {};
+  int64_t pcnt[MUON_KIND_COUNT] = {};
+};
+
+namespace {
+
+DevMat make_devmat(const muon_plan* p, int i) {
+  const Geometry& g = p->geo[i];
+  const muon_matrix_desc& d = p->desc[i];
+  const Layout::M& m = p->lay.m[i];
+  DevMat r;
+  std::memset(&r, 0, sizeof(r));
+  r.w = d.weight;
+  r.g = d.grad;
+  r.mom = d.momentum;
+  r.x32 = m.x32 == (size_t)-1 ? nullptr : (float*)(p->ws + m.x32);
+  r.xo[0] = p->ws + m.xo0;
+  r.xo[1] = p->ws + m.xo1;
+  r.a = p->ws + m.a;
+  r.b = p->ws + m.b;
+  r.part = (float*)(p->ws + m.part);
+  r.sc = (float*)(p->ws + m.sc);
+  r.rows = g.rows;
+  r.cols = g.cols;
+  r.m = g.m;
+  r.n = g.n;
+  r.mp = g.mp;
+  r.np = g.np;
+  r.transposed = g.tr;
+  r.w_bf16 = d.w_dtype == MUON_DTYPE_BF16;
+  r.g_bf16 = d.g_dtype == MUON_DTYPE_BF16;
+  r.nparts = g.nparts;
+  r.mom_tiles_n = g.mom_n;
+  r.scale = d.scale > 0.f ? d.scale : 1.f;
+  r.vec_g = (g.cols % 4 == 0) && ((uintptr_t)d.grad % 16 == 0) && ((uintptr_t)d.momentum % 16 == 0);
+  r.vec_w = (g.cols % 4 == 0) && ((uintptr_t)d.weight % 16 == 0);
+  r.f32 = g.f32;
+  return r;
+}
+
+DevMat* slot_ptr(const muon_plan* p, int s) { return (DevMat*)(p->ws + p->lay.slots + p->lay.slot_bytes * s); }
+
+// Upload the host image of the matrix table into the next device slot.
+int upload_table(muon_plan* p, hipStream_t stream) {
+  const int s = (p->slot + 1) % kSlots;
+  if (p->slot_used[s]) {
+    hipError_t e = hipEventSynchronize(p->slot_ev[s]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(table slot)");
+  }
+  std::memcpy(p->host_slots[s], p->hmat.data(), sizeof(DevMat) * p->n);
+  hipError_t e = hipMemcpyAsync(slot_ptr(p, s), p->host_slots[s], sizeof(DevMat) * p->n, hipMemcpyHostToDevice,
+                                stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(matrix table)");
+  p->slot = s;
+  return MUON_OK;
+}
+
+int note_slot_use(muon_plan* p, hipStream_t stream) {
+  hipError_t e = hipEventRecord(p->slot_ev[p->slot], stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(table slot)");
+  p->slot_used[p->slot] = true;
+  e = hipEventRecord(p->last_ev, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  p->last_valid = true;
+  return MUON_OK;
+}
+
+int prof_begin(muon_plan* p, int kind, hipStream_t stream, size_t* idx) {
+  if (!p->prof) return MUON_OK;
+  if (p->pused * 2 + 2 > p->pev.size()) {
+    for (int k = 0; k < 64; ++k) {
+      hipEvent_t ev;
+      hipError_t e = hipEventCreate(&ev);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+      p->pev.push_back(ev);
+    }
+  }
+  *idx = p->pused++;
+  if (p->pkind.size() < p->pused) p->pkind.resize(p->pused);
+  p->pkind[*idx] = kind;
+  hipError_t e = hipEventRecord(p->pev[2 * *idx], stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(profile)");
+  return MUON_OK;
+}
+
+int prof_end(muon_plan* p, hipStream_t stream, size_t idx) {
+  if (!p->prof) return MUON_OK;
+  hipError_t e = hipEventRecord(p->pev[2 * idx + 1], stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(profile)");
+  return MUON_OK;
+}
+
+int check_launch(hipError_t e, const char* what) {
+  if (e != hipSuccess) return hip_fail(e, what);
+  return MUON_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* muon_version(void) { return "muon-mi355x 1.0.0 (gfx950)"; }
+
+const char* muon_last_error(void) { return g_err.c_str(); }
+
+size_t muon_workspace_size(const muon_matrix_desc* descs, int n, const muon_options* opts) {
+  Options o;
+  if (read_options(opts, &o)) return 0;
+  if (validate_all(descs, n, false)) return 0;
+  std::vector<Geometry> geo(n);
+  for (int i = 0; i < n; ++i) geo[i] = geometry(descs[i], o.path);
+  Tables t = build_tables(geo);
+  Layout L;
+  return layout(geo, o, t, &L);
+}
+
+int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts, muon_plan_info* info, int kind,
+                  int32_t* tiles, int tile_cap, int32_t* n_tiles) {
+  g_err.clear();
+  Options o;
+  int rc = read_options(opts, &o);
+  if (rc) return rc;
+  rc = validate_all(descs, n, false);
+  if (rc) return rc;
+  std::vector<Geometry> geo(n);
+  for (int i = 0; i < n; ++i) geo[i] = geometry(descs[i], o.path);
+  Tables t = build_tables(geo);
+  Layout L;
+  const size_t total = layout(geo, o, t, &L);
+  if (info) {
+    info->workspace_bytes = (int64_t)total;
+    info->n_matrices = n;
+    info->tile = kTile;
+    info->blocks[MUON_KIND_MOMENTUM] = (int32_t)t.mom.size();
+    info->blocks[MUON_KIND_GRAM] = (int32_t)(t.ns[0][kGram].size() + t.ns[1][kGram].size());
+    info->blocks[MUON_KIND_POLY] = (int32_t)(t.ns[0][kPoly].size() + t.ns[1][kPoly].size());
+    info->blocks[MUON_KIND_UPDATE] = (int32_t)(t.ns[0][kUpd].size() + t.ns[1][kUpd].size());
+    info->blocks[MUON_KIND_APPLY] = (int32_t)t.mom.size();
+    info->x_master_iters = o.kmaster;
+    info->path = o.path;
+    int nf = 0;
+    for (const Geometry& g : geo) nf += g.f32;
+    info->n_f32_matrices = nf;
+  }
+  if (kind >= 0) {
+    std::vector<Tile> v;
+    switch (kind) {
+      case MUON_KIND_MOMENTUM:
+      case MUON_KIND_APPLY: v = t.mom; break;
+      case MUON_KIND_GRAM:
+      case MUON_KIND_POLY:
+      case MUON_KIND_UPDATE: {
+        const int k = kind == MUON_KIND_GRAM ? kGram : kind == MUON_KIND_POLY ? kPoly : kUpd;
+        v = t.ns[0][k];
+        v.insert(v.end(), t.ns[1][k].begin(), t.ns[1][k].end());
+        break;
+      }
+      default: return fail(MUON_E_INVAL, "kind %d unknown", kind);
+    }
+    if (n_tiles) *n_tiles = (int32_t)v.size();
+    if (tiles) {
+      const int cnt = std::min<int>(tile_cap, (int)v.size());
+      for (int q = 0; q < cnt; ++q) {
+        const Tile& tl = v[q];
+        tiles[3 * q] = tl.mat == kNullMat ? -1 : tl.mat;
+        tiles[3 * q + 1] = tl.ti;
+        tiles[3 * q + 2] = tl.tj;
+      }
+    }
+  }
+  return MUON_OK;
+}
+
+int muon_init(const muon_matrix_desc* descs, int n, const muon_options* opts, void* workspace, size_t ws_bytes,
+              void* hip_stream, muon_plan** out_plan) {
+  g_err.clear();
+  if (!out_plan) return fail(MUON_E_INVAL, "out_plan is NULL");
+  *out_plan = nullptr;
+  Options o;
+  int rc = read_options(opts, &o);
+  if (rc) return rc;
+  rc = validate_all(descs, n, true);
+  if (rc) return rc;
+  if (!workspace) return fail(MUON_E_WORKSPACE, "workspace is NULL");
+  if ((uintptr_t)workspace % kAlign) return fail(MUON_E_WORKSPACE, "workspace is not 256-byte aligned");
+
+  muon_plan* p = new (std::nothrow) muon_plan();
+  if (!p) return fail(MUON_E_INVAL, "out of host memory");
+  p->n = n;
+  p->opt = o;
+  p->desc.assign(descs, descs + n);
+  p->geo.resize(n);
+  for (int i = 0; i < n; ++i) p->geo[i] = geometry(descs[i], o.path);
+  p->tab = build_tables(p->geo);
+  const size_t need = layout(p->geo, o, p->tab, &p->lay);
+  if (ws_bytes < need) {
+    delete p;
+    return fail(MUON_E_WORKSPACE, "workspace has %zu bytes, the plan needs %zu", ws_bytes, need);
+  }
+  p->ws = (char*)workspace;
+  p->ws_bytes = ws_bytes;
+  hipStream_t stream = (hipStream_t)hip_stream;
+
+  auto cleanup = [&](int code) {
+    muon_destroy(p);
+    return code;
+  };
+  for (int s = 0; s < kSlots; ++s) {
+    hipError_t e = hipHostMalloc((void**)&p->host_slots[s], sizeof(DevMat) * n, hipHostMallocDefault);
+    if (e != hipSuccess) return cleanup(hip_fail(e, "hipHostMalloc(table staging)"));
+    e = hipEventCreateWithFlags(&p->slot_ev[s], hipEventDisableTiming);
+    if (e != hipSuccess) return cleanup(hip_fail(e, "hipEventCreate"));
+  }
+  hipError_t e = hipEventCreateWithFlags(&p->last_ev, hipEventDisableTiming);
+  if (e != hipSuccess) return cleanup(hip_fail(e, "hipEventCreate"));
+
+  // Tile tables: staged through pinned memory, uploaded once; init waits for
+  // them so the staging can be released.
+  std::vector<std::pair<const std::vector<Tile>*, size_t>> lists;
+  lists.push_back({&p->tab.mom, p->lay.mom_tiles});
+  for (int prec = 0; prec < 2; ++prec)
+    for (int k = 0; k < 3; ++k) lists.push_back({&p->tab.ns[prec][k], p->lay.ns_tiles[prec][k]});
+  size_t tb = 0;
+  for (auto& l : lists) tb += sizeof(Tile) * l.first->size();
+  void* stage = nullptr;
+  e = hipHostMalloc(&stage, std::max<size_t>(tb, 16), hipHostMallocDefault);
+  if (e != hipSuccess) return cleanup(hip_fail(e, "hipHostMalloc(tile staging)"));
+  char* sp = (char*)stage;
+  for (auto& l : lists) {
+    const size_t bytes = sizeof(Tile) * l.first->size();
+    if (!bytes) continue;
+    std::memcpy(sp, l.first->data(), bytes);
+    e = hipMemcpyAsync(p->ws + l.second, sp, bytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) {
+      (void)hipHostFree(stage);
+      return cleanup(hip_fail(e, "hipMemcpyAsync(tile tables)"));
+    }
+    sp += bytes;
+  }
+  p->hmat.resize(n);
+  for (int i = 0; i < n; ++i) p->hmat[i] = make_devmat(p, i);
+  p->slot = kSlots - 1;
+  rc = upload_table(p, stream);
+  if (rc) {
+    (void)hipHostFree(stage);
+    return cleanup(rc);
+  }
+  if (o.zero) {
+    for (int i = 0; i < n; ++i) {
+      e = hipMemsetAsync(descs[i].momentum, 0, sizeof(float) * descs[i].rows * descs[i].cols, stream);
+      if (e != hipSuccess) {
+        (void)hipHostFree(stage);
+        return cleanup(hip_fail(e, "hipMemsetAsync(momentum)"));
+      }
+    }
+  }
+  e = hipStreamSynchronize(stream);
+  (void)hipHostFree(stage);
+  if (e != hipSuccess) return cleanup(hip_fail(e, "hipStreamSynchronize(init upload)"));
+  *out_plan = p;
+  return MUON_OK;
+}
+
+int muon_step(muon_plan* p, const muon_matrix_desc* descs, int n, float a, float b, float c, int T, float momentum,
+              int nesterov, float lr, void* hip_stream) {
+  g_err.clear();
+  if (!p) return fail(MUON_E_INVAL, "plan is NULL");
+  if (T < 0 || T > p->opt.maxT) return fail(MUON_E_INVAL, "T=%d outside [0, max_T=%d]", T, p->opt.maxT);
+  if (!std::isfinite(a) || !std::isfinite(b) || !std::isfinite(c) || !std::isfinite(lr))
+    return fail(MUON_E_INVAL, "a, b, c and lr must be finite");
+  if (!(momentum >= 0.f && momentum <= 1.f)) return fail(MUON_E_INVAL, "momentum %g outside [0, 1]", momentum);
+  hipStream_t stream = (hipStream_t)hip_stream;
+
+  bool changed = false;
+  if (descs) {
+    if (n != p->n) return fail(MUON_E_MISMATCH, "step has %d matrices, the plan %d", n, p->n);
+    int rc = validate_all(descs, n, true);
+    if (rc) return rc;
+    for (int i = 0; i < n; ++i) {
+      const muon_matrix_desc& x = descs[i];
+      const muon_matrix_desc& y = p->desc[i];
+      if (x.rows != y.rows || x.cols != y.cols || x.g_dtype != y.g_dtype || x.w_dtype != y.w_dtype ||
+          x.scale != y.scale)
+        return fail(MUON_E_MISMATCH, "matrix %d: shape, dtype or scale differs from the plan", i);
+      if (x.weight != y.weight || x.grad != y.grad || x.momentum != y.momentum) changed = true;
+    }
+    if (changed) {
+      for (int i = 0; i < n; ++i) {
+        p->desc[i].weight = descs[i].weight;
+        p->desc[i].grad = descs[i].grad;
+        p->desc[i].momentum = descs[i].momentum;
+        p->hmat[i] = make_devmat(p, i);
+      }
+      int rc2 = upload_table(p, stream);
+      if (rc2) return rc2;
+    }
+  }
+
+  const DevMat* mats = slot_ptr(p, p->slot);
+  const Tile* mom_tiles = (const Tile*)(p->ws + p->lay.mom_tiles);
+  const int nmom = (int)p->tab.mom.size();
+
+  size_t pi = 0;
+  int rc;
+  MomArgs ma{mats, mom_tiles, momentum, nesterov ? 1 : 0};
+  if ((rc = prof_begin(p, MUON_KIND_MOMENTUM, stream, &pi))) return rc;
+  if ((rc = check_launch(launch_momentum(ma, nmom, stream), "momentum launch"))) return rc;
+  if ((rc = prof_end(p, stream, pi))) return rc;
+
+  if (T == 0) {
+    ApplyArgs aa{mats, mom_tiles, lr};
+    if ((rc = prof_begin(p, MUON_KIND_APPLY, stream, &pi))) return rc;
+    if ((rc = check_launch(launch_apply(aa, nmom, stream), "apply launch"))) return rc;
+    if ((rc = prof_end(p, stream, pi))) return rc;
+  }
+  static const int kKinds[3] = {MUON_KIND_GRAM, MUON_KIND_POLY, MUON_KIND_UPDATE};
+  static const char* kNames[3] = {"gram launch", "poly launch", "update launch"};
+  for (int t = 1; t <= T; ++t) {
+    for (int k = 0; k < 3; ++k) {
+      for (int prec = 0; prec < 2; ++prec) {
+        const int blocks = (int)p->tab.ns[prec][k].size();
+        if (!blocks) continue;
+        StageArgs sa{mats, (const Tile*)(p->ws + p->lay.ns_tiles[prec][k]), t, T, p->opt.kmaster, a, b, c, lr};
+        if ((rc = prof_begin(p, kKinds[k], stream, &pi))) return rc;
+        if ((rc = check_launch(launch_stage(k + 1, prec == 1, sa, blocks, stream), kNames[k]))) return rc;
+        if ((rc = prof_end(p, stream, pi))) return rc;
+      }
+    }
+  }
+  return note_slot_use(p, stream);
+}
+
+int muon_destroy(muon_plan* p) {
+  g_err.clear();
+  if (!p) return MUON_OK;
+  if (p->last_valid) (void)hipEventSynchronize(p->last_ev);
+  for (int s = 0; s < kSlots; ++s) {
+    if (p->host_slots[s]) (void)hipHostFree(p->host_slots[s]);
+    if (p->slot_ev[s]) (void)hipEventDestroy(p->slot_ev[s]);
+  }
+  if (p->last_ev) (void)hipEventDestroy(p->last_ev);
+  for (hipEvent_t ev : p->pev) (void)hipEventDestroy(ev);
+  delete p;
+  return MUON_OK;
+}
+
+int muon_profile_enable(muon_plan* p, int enable) {
+  g_err.clear();
+  if (!p) return fail(MUON_E_INVAL, "plan is NULL");
+  p->prof = enable != 0;
+  return MUON_OK;
+}
+
+int muon_profile_read(muon_plan* p, double* ms, int64_t* launches) {
+  g_err.clear();
+  if (!p) return fail(MUON_E_INVAL, "plan is NULL");
+  for (size_t q = 0; q < p->pused; ++q) {
+    hipError_t e = hipEventSynchronize(p->pev[2 * q + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(profile)");
+    float t = 0.f;
+    e = hipEventElapsedTime(&t, p->pev[2 * q], p->pev[2 * q + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    p->pms[p->pkind[q]] += t;
+    p->pcnt[p->pkind[q]] += 1;
+  }
+  p->pused = 0;
+  for (int k = 0; k < MUON_KIND_COUNT; ++k) {
+    if (ms) ms[k] = p->pms[k];
+    if (launches) launches[k] = p->pcnt[k];
+    p->pms[k] = 0.0;
+    p->pcnt[k] = 0;
+  }
+  return MUON_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Internal layout shared by the host planner and the gfx950 kernels.
+//
+// Every matrix is handled in its canonical orientation X (m x n, m <= n):
+// X = U when rows <= cols, X = U^T otherwise.  All workspace buffers of a
+// matrix are padded to whole NS tiles (multiples of kTile in both
+// dimensions).  The padding is zero in X0 (the momentum kernel writes it) and
+// the iteration keeps it zero exactly (zero rows/columns stay zero under
+// X X^T, b A + c A A and a X + B X), so the product kernels need no bounds
+// checks; only the final weight step looks at the true extents.
+#pragma once
+
+#include <stdint.h>
+
+namespace muon {
+
+constexpr int kTile = 128;     // NS product tile edge (rows and columns)
+constexpr int kMomTile = 64;   // momentum kernel tile edge
+constexpr int kThreads = 256;  // threads per block, every kernel
+constexpr int kXcds = 8;       // MI355X: 8 XCDs, blocks dispatched round-robin
+constexpr uint16_t kNullMat = 0xFFFF;  // tile-table filler: the block exits
+constexpr double kEps = 1e-7;
+// On the bf16 path, matrices whose short side is below this run the fp32
+// arithmetic: with so few terms in the A*A and B*X contractions the bf16
+// operand rounding does not average out (4x8 inputs reach 2-5e-2 relative
+// error in bf16), while their cost is negligible.
+constexpr int kMinBf16Side = 64;
+
+// One matrix, as the kernels see it.
+struct DevMat {
+  void* w;            // weights (rows x cols), f32 or bf16
+  const void* g;      // gradient (rows x cols), f32 or bf16
+  float* mom;         // momentum (rows x cols), f32
+  float* x32;         // bf16 path: fp32 master copy of X (mp x np); else null
+  void* xo[2];        // operand copies of X (ping-pong), bf16 or f32, mp x np
+  void* a;            // A = X X^T, mp x mp (bf16 or f32)
+  void* b;            // B = b A + c A A, mp x mp
+  float* part;        // momentum-kernel partial sums of squares, one per tile
+  float* sc;          // [0] = 1/(||U||_F + eps), [1] = ||U||_F
+  int32_t rows, cols; // original shape
+  int32_t m, n;       // canonical shape (m <= n)
+  int32_t mp, np;     // padded canonical shape
+  int32_t transposed; // rows > cols
+  int32_t w_bf16;     // weight dtype is bf16
+  int32_t g_bf16;     // gradient dtype is bf16
+  int32_t nparts;     // number of momentum tiles (= partial sums)
+  int32_t mom_tiles_n;// momentum tiles along the canonical n axis
+  float scale;        // s of the weight step (already defaulted to 1)
+  int32_t vec_g;      // gradient rows can be read 4 elements at a time
+  int32_t vec_w;      // weight rows can be read/written 4 elements at a time
+  int32_t f32;        // this matrix's products use fp32 operands (xo, a, b are fp32)
+  int32_t pad_;
+};
+
+struct Tile {
+  uint16_t mat;  // matrix index, kNullMat for filler
+  uint16_t ti;   // tile row
+  uint16_t tj;   // tile column
+  uint16_t pad;
+};
+
+struct StageArgs {
+  const DevMat* mats;
+  const Tile* tiles;
+  int32_t t;        // iteration, 1-based
+  int32_t T;        // iterations this step
+  int32_t kmaster;  // bf16 path: iterations 1..kmaster read the fp32 master in a*X
+  float a, b, c;
+  float lr;
+};
+
+struct MomArgs {
+  const DevMat* mats;
+  const Tile* tiles;
+  float mu;
+  int32_t nesterov;
+};
+
+struct ApplyArgs {
+  const DevMat* mats;
+  const Tile* tiles;
+  float lr;
+};
+
+}  // namespace muon

@@ -1,0 +1,201 @@
+"""The C ABI library on the host (no GPU): exports, planning, validation and error paths.
+
+Nothing here launches a kernel; every call either is host-only
+(muon_version, muon_workspace_size, muon_describe, muon_last_error) or is
+rejected by argument validation before any HIP call is made.
+"""
+import ctypes
+import os
+import re
+from collections import Counter
+
+import pytest
+
+from muon_newton_schulz_03_amd import _lib, describe, inputs
+from muon_newton_schulz_03_amd._lib import MatrixDesc, Options
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from muon_newton_schulz_03_amd.build import build_library
+        build_library()
+    return _lib.load()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "muon.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muon_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version(lib):
+    assert lib.muon_version().decode().startswith("muon-mi355x")
+
+
+def descs(shapes, ptrs=False, **kw):
+    arr = (MatrixDesc * len(shapes))()
+    for i, (r, c) in enumerate(shapes):
+        d = arr[i]
+        d.rows, d.cols, d.ld_w, d.ld_g = r, c, c, c
+        d.w_dtype = kw.get("w_dtype", _lib.MUON_DTYPE_F32)
+        d.g_dtype = kw.get("g_dtype", _lib.MUON_DTYPE_BF16)
+        if ptrs:
+            base = 0x100000 * (i + 1)
+            d.weight, d.grad, d.momentum = base, base + 0x40000, base + 0x80000
+    return arr
+
+
+def test_workspace_size_model(lib):
+    # 768x768 bf16 path, fp32 master: X32 + 2 bf16 X + A + B, each 256-aligned, plus tables
+    arr = descs([(768, 768)])
+    ws = lib.muon_workspace_size(arr, 1, None)
+    x = 768 * 768
+    assert ws >= x * 4 + 2 * x * 2 + 2 * x * 2
+    assert ws < x * 4 + 4 * x * 2 + 1 << 20
+    # no master copy: 4 bytes per element less
+    ws0 = lib.muon_workspace_size(arr, 1, ctypes.byref(Options(0, 0, 0, 0)))
+    assert ws - ws0 == x * 4
+    # fp32 path: 4-byte operands, no master
+    wsf = lib.muon_workspace_size(arr, 1, ctypes.byref(Options(1, -1, 0, 0)))
+    assert wsf - ws0 == 4 * x * 2
+    g = inputs.workload("gpt2_small")
+    d, _ = describe(g.shapes)
+    assert 0.84e9 < d["workspace_bytes"] < 0.86e9
+
+
+@pytest.mark.parametrize("shapes", [[(768, 768)], [(4, 8), (8, 4), (1, 1), (257, 129), (130, 1000)],
+                                    inputs.workload("gpt2_small").shapes[:12]])
+def test_tile_lists_cover_each_tile_once(shapes):
+    for kind in (_lib.KIND_MOMENTUM, _lib.KIND_GRAM, _lib.KIND_POLY, _lib.KIND_UPDATE):
+        info, tiles = describe(shapes, kind=kind)
+        real = [t for t in tiles if t[0] >= 0]
+        cnt = Counter(real)
+        assert all(v == 1 for v in cnt.values())
+        expect = set()
+        for i, (r, c) in enumerate(shapes):
+            m, n = min(r, c), max(r, c)
+            mp, np_ = -(-m // 128) * 128, -(-n // 128) * 128
+            if kind == _lib.KIND_MOMENTUM:
+                expect |= {(i, a, b) for a in range(mp // 64) for b in range(np_ // 64)}
+            elif kind == _lib.KIND_UPDATE:
+                expect |= {(i, a, b) for a in range(mp // 128) for b in range(np_ // 128)}
+            else:
+                expect |= {(i, a, b) for a in range(mp // 128) for b in range(a, mp // 128)}
+        assert set(cnt) == expect
+        assert info["blocks"][kind] == len(tiles)
+
+
+def test_xcd_runs_are_balanced():
+    g = inputs.workload("gpt2_small")
+    for kind in (_lib.KIND_GRAM, _lib.KIND_POLY, _lib.KIND_UPDATE):
+        _, tiles = describe(g.shapes, kind=kind)
+        load = Counter()
+        for b, (mat, ti, tj) in enumerate(tiles):
+            if mat < 0:
+                continue
+            r, c = g.shapes[mat]
+            load[b % 8] += max(r, c) if kind == _lib.KIND_GRAM else min(r, c)
+        assert max(load.values()) / min(load.values()) < 1.02
+        # each XCD works on a contiguous run of matrices: a matrix spans at most 2 XCDs
+        xcds = {}
+        for b, (mat, _, _) in enumerate(tiles):
+            if mat >= 0:
+                xcds.setdefault(mat, set()).add(b % 8)
+        assert max(len(v) for v in xcds.values()) <= 2
+
+
+def test_short_matrices_take_fp32_products():
+    d, _ = describe([(4, 8), (63, 1000), (64, 64), (768, 768), (3000, 40)])
+    assert d["n_f32_matrices"] == 3
+    d, _ = describe([(4, 8), (768, 768)], path="f32")
+    assert d["n_f32_matrices"] == 2
+    # each precision has its own launch: the lists hold both sets of tiles
+    _, tiles = describe([(4, 8), (768, 768)], kind=_lib.KIND_UPDATE)
+    assert {t[0] for t in tiles if t[0] >= 0} == {0, 1}
+
+
+def test_master_iters_option():
+    d, _ = describe([(64, 64)], x_master_iters=-1)
+    assert d["x_master_iters"] == 3
+    d, _ = describe([(64, 64)], x_master_iters=5)
+    assert d["x_master_iters"] == 5
+    d, _ = describe([(64, 64)], path="f32")
+    assert d["x_master_iters"] == 0
+
+
+def expect_error(code, fn, *args, match=None):
+    rc = fn(*args)
+    assert rc == code, (rc, _lib.last_error())
+    if match:
+        assert re.search(match, _lib.last_error()), _lib.last_error()
+
+
+def test_validation_errors(lib):
+    plan = ctypes.c_void_p()
+    ws = ctypes.c_void_p(0x10000000)  # never touched: validation fails first
+    E = _lib
+    expect_error(E.MUON_E_INVAL, lib.muon_init, None, 1, None, ws, 1 << 30, None, ctypes.byref(plan))
+    expect_error(E.MUON_E_INVAL, lib.muon_init, descs([(4, 4)], True), 0, None, ws, 1 << 30, None,
+                 ctypes.byref(plan), match="count")
+    bad = descs([(4, 4)], True)
+    bad[0].rows = 0
+    expect_error(E.MUON_E_INVAL, lib.muon_init, bad, 1, None, ws, 1 << 30, None, ctypes.byref(plan),
+                 match="positive")
+    bad = descs([(4, 4)], True)
+    bad[0].ld_g = 8
+    expect_error(E.MUON_E_UNSUPPORTED, lib.muon_init, bad, 1, None, ws, 1 << 30, None, ctypes.byref(plan),
+                 match="ld_g")
+    bad = descs([(4, 4)], True, g_dtype=7)
+    expect_error(E.MUON_E_UNSUPPORTED, lib.muon_init, bad, 1, None, ws, 1 << 30, None, ctypes.byref(plan))
+    bad = descs([(4, 4)], False)
+    expect_error(E.MUON_E_INVAL, lib.muon_init, bad, 1, None, ws, 1 << 30, None, ctypes.byref(plan),
+                 match="null")
+    bad = descs([(4, 4)], True)
+    bad[0].grad = bad[0].weight
+    expect_error(E.MUON_E_INVAL, lib.muon_init, bad, 1, None, ws, 1 << 30, None, ctypes.byref(plan),
+                 match="distinct")
+    bad = descs([(4, 4)], True)
+    bad[0].scale = float("nan")
+    expect_error(E.MUON_E_INVAL, lib.muon_init, bad, 1, None, ws, 1 << 30, None, ctypes.byref(plan))
+    bad = descs([(4, 4)], True)
+    bad[0].reserved = 1
+    expect_error(E.MUON_E_INVAL, lib.muon_init, bad, 1, None, ws, 1 << 30, None, ctypes.byref(plan))
+    ok = descs([(4, 4)], True)
+    expect_error(E.MUON_E_WORKSPACE, lib.muon_init, ok, 1, None, None, 1 << 30, None, ctypes.byref(plan))
+    expect_error(E.MUON_E_WORKSPACE, lib.muon_init, ok, 1, None, ctypes.c_void_p(0x10000010), 1 << 30, None,
+                 ctypes.byref(plan), match="aligned")
+    expect_error(E.MUON_E_WORKSPACE, lib.muon_init, ok, 1, None, ws, 1024, None, ctypes.byref(plan),
+                 match="needs")
+    expect_error(E.MUON_E_UNSUPPORTED, lib.muon_init, ok, 1, ctypes.byref(Options(9, 0, 0, 0)), ws, 1 << 30,
+                 None, ctypes.byref(plan))
+    expect_error(E.MUON_E_INVAL, lib.muon_init, ok, 1, None, ws, 1 << 30, None, None)
+    assert not plan.value
+    assert lib.muon_workspace_size(bad, 1, None) == 0
+
+
+def test_step_and_destroy_on_null_plan(lib):
+    expect_error(_lib.MUON_E_INVAL, lib.muon_step, None, None, 0, 1.0, 1.0, 1.0, 5, 0.9, 1, 0.1, None,
+                 match="plan")
+    assert lib.muon_destroy(None) == 0
+    expect_error(_lib.MUON_E_INVAL, lib.muon_profile_enable, None, 1)
+    expect_error(_lib.MUON_E_INVAL, lib.muon_profile_read, None, None, None)
+    # errors are per thread and cleared by the next successful call
+    assert lib.muon_destroy(None) == 0 and _lib.last_error() == ""
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    from muon_newton_schulz_03_amd import MuonStep
+    w = torch.zeros(4, 4)
+    with pytest.raises(ValueError, match="device"):
+        MuonStep([w], [w.clone()], [w.clone()])
