@@ -1,0 +1,212 @@
+"""Benchmark of the MI355X Muon step on the GPT-2 small hidden-matrix set.
+
+One step = the whole hot path over all 72 hidden matrices of the 12-layer,
+width-768 GPT-2 small model (overview page "The NanoGPT speedrun",
+paragraph "Context"): momentum + Nesterov + Frobenius norm, T = 5 quintic
+Newton-Schulz iterations, weight update, on fresh seeded bf16 gradients each
+step (already resident in HBM; the plan is handed each step's gradient
+buffers).  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+WORKLOAD = "gpt2_small"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "muon_newton_schulz_03_amd", "csrc", f)
+                  for f in ("kernels.hip", "muon_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def work_model(shapes, T):
+    """Algorithmic FLOPs per launch kind and step (distinct entries of the symmetric products)."""
+    gram = poly = upd = 0
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        gram += m * (m + 1) * n
+        poly += m * m * (m + 1)
+        upd += 2 * m * m * n
+    dense = sum(T * (4 * min(r, c) ** 2 * max(r, c) + 2 * min(r, c) ** 3) for r, c in shapes)
+    return {"gram": gram, "poly": poly, "update": upd, "step": T * (gram + poly + upd), "dense_step": dense}
+
+
+def momentum_bytes(shapes, master: bool):
+    """Algorithmic HBM bytes of the momentum kernel: G (bf16) + M read/write + X0 (bf16 [+ fp32])."""
+    p = sum(r * c for r, c in shapes)
+    return p * (2 + 4 + 4 + 2 + (4 if master else 0))
+
+
+def read_traffic(kind: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if still current."""
+    path = os.path.join(PROFILES, f"{kind}_{WORKLOAD}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = (s.strip() for s in line.split("=", 1))
+                vals[k] = v
+    if vals.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, budget_s: float = 12.0):
+    """Time the fp64 oracle (as it stands) on a bounded sample: layer 0's six matrices, one step each."""
+    import numpy as np
+    import torch
+
+    from muon_newton_schulz_03_amd import inputs
+    from oracle import muon_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=os.cpu_count())
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    idx = list(range(6))
+    grads = inputs.gradients(WORKLOAD, 0, indices=idx)
+    zeros = [np.zeros(wl.shapes[i]) for i in idx]
+    mz = [np.zeros(wl.shapes[i], np.float32) for i in idx]
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for k, i in enumerate(idx):
+            O.muon_step(zeros[k], grads[k], mz[k], a=wl.coeffs[0], b=wl.coeffs[1], c=wl.coeffs[2], T=wl.T,
+                        mu=wl.momentum, nesterov=wl.nesterov, lr=wl.lr)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 50:
+            break
+    layers = len(wl.shapes) // 6
+    steps_per_s = reps / (el * layers)
+    return {"value": steps_per_s, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"layer 0 (6 of 72 matrices: 4x768x768, 768x3072, 3072x768), {reps} oracle step(s) "
+                      f"in {el:.1f} s, scaled by 12 layers"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--x-master-iters", type=int, default=-1)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the Muon step here has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from muon_newton_schulz_03_amd import MuonStep, inputs
+
+    wl = inputs.workload(WORKLOAD)
+    dev = torch.device("cuda:0")
+    n = len(wl.shapes)
+    total = args.warmup + args.steps
+    print(f"[bench] {WORKLOAD}: {n} matrices, {wl.params} params, {total} gradient sets", file=sys.stderr,
+          flush=True)
+    grads = [inputs.gradients(WORKLOAD, t, device=dev) for t in range(total)]
+    W = inputs.weights(wl.shapes, seed=11, device=dev)
+    M = [torch.zeros(s, dtype=torch.float32, device=dev) for s in wl.shapes]
+    plan = MuonStep(W, grads[0], M, x_master_iters=args.x_master_iters)
+    kw = dict(a=wl.coeffs[0], b=wl.coeffs[1], c=wl.coeffs[2], T=wl.T, momentum=wl.momentum,
+              nesterov=wl.nesterov, lr=wl.lr)
+    for t in range(args.warmup):
+        plan.step(grads=grads[t], **kw)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, per-launch HIP events recorded by the library on this stream
+    plan.profile(True)
+    plan.read_profile()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for t in range(args.warmup, total):
+        plan.step(grads=grads[t], **kw)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    prof = plan.read_profile()
+    plan.profile(False)
+    plan.close()
+
+    ms_step = ms_total / args.steps
+    steps_per_s = 1000.0 / ms_step
+    work = work_model(wl.shapes, wl.T)
+    tflops = work["step"] * steps_per_s / 1e12
+    per_kind = {k: {"ms_per_launch": v[0] / v[1], "launches": v[1]} for k, v in prof.items() if v[1]}
+    for k in ("gram", "poly", "update"):
+        if k in per_kind:
+            per_kind[k]["tflops"] = work[k] / (per_kind[k]["ms_per_launch"] * 1e-3) / 1e12
+    if "momentum" in per_kind:
+        per_kind["momentum"]["gbs"] = momentum_bytes(wl.shapes, True) / (per_kind["momentum"]["ms_per_launch"]
+                                                                          * 1e-3) / 1e9
+    dom = max(("gram", "poly", "update", "momentum"), key=lambda k: prof[k][0])
+    if dom == "momentum":
+        achieved = per_kind[dom]["gbs"]
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    else:
+        achieved = per_kind[dom]["tflops"]
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS}
+    roof["kernel"] = dom
+    roof["traffic"] = read_traffic(dom)
+
+    out = {
+        "metric": "Muon steps/s on GPT-2-small hidden set (T=5); % bf16 MFMA peak",
+        "value": steps_per_s,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gpt2_small_hidden_72", "matrices": n, "params": wl.params, "T": wl.T,
+                   "grad_dtype": "bf16", "weight_dtype": "f32", "momentum": wl.momentum, "nesterov": True,
+                   "lr": wl.lr, "coeffs": list(wl.coeffs)},
+        "tflops_algorithmic": tflops,
+        "frac_bf16_peak": tflops / PEAK_BF16_TFLOPS,
+        "tflops_dense_model": work["dense_step"] * steps_per_s / 1e12,
+        "matrices_per_s": n * steps_per_s,
+        "kernels": per_kind,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

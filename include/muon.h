@@ -119,7 +119,7 @@ int muon_init(const muon_matrix_desc* descs, int n, const muon_options* opts,
               void* workspace, size_t ws_bytes, void* hip_stream, muon_plan** out_plan);
 
 /* Enqueue one Muon step over every matrix of the plan on hip_stream:
- * 1 momentum/norm launch, then 3 launches per Newton-Schulz iteration (all
+ * 1 momentum launch and 1 norm launch, then 3 launches per Newton-Schulz iteration (all
  * matrices of one precision grouped in each launch: 6 per iteration when the
  * plan mixes bf16 and fp32 matrices); T == 0 enqueues one weight-step launch
  * instead (W <- W - lr*s*X0).  descs == NULL reuses the pointers the plan
@@ -143,7 +143,8 @@ const char* muon_last_error(void);
 #define MUON_KIND_POLY 2     /* B = b A + c A A (upper tiles, mirrored) */
 #define MUON_KIND_UPDATE 3   /* X <- a X + B X; on the last iteration W <- W - lr s O */
 #define MUON_KIND_APPLY 4    /* T == 0 only: W <- W - lr s X0 */
-#define MUON_KIND_COUNT 5
+#define MUON_KIND_NORM 5     /* T > 0: 1 / (||U||_F + eps) per matrix from the momentum partials */
+#define MUON_KIND_COUNT 6
 
 /* Host-only description of the plan these descriptors would get.  Returns
  * MUON_OK and fills the fields, or an error code.  `tiles` (optional) gets
@@ -153,7 +154,10 @@ typedef struct muon_plan_info {
   int64_t workspace_bytes;
   int32_t n_matrices;
   int32_t tile;              /* tile edge of the Newton-Schulz products */
-  int32_t blocks[MUON_KIND_COUNT]; /* grid size of each launch kind */
+  int32_t blocks[MUON_KIND_COUNT]; /* tile-table length of each launch kind: the grid of
+                                      the momentum, norm and apply launches; the product
+                                      kernels are persistent (2 blocks per CU) and
+                                      stride through their table */
   int32_t x_master_iters;
   int32_t path;
   int32_t n_f32_matrices;    /* matrices whose products run in fp32 (see below) */

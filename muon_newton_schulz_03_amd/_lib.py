@@ -19,9 +19,9 @@ MUON_DTYPE_BF16 = 1
 MUON_PATH_BF16 = 0
 MUON_PATH_F32 = 1
 
-KIND_MOMENTUM, KIND_GRAM, KIND_POLY, KIND_UPDATE, KIND_APPLY = range(5)
-KIND_COUNT = 5
-KIND_NAMES = ("momentum", "gram", "poly", "update", "apply")
+KIND_MOMENTUM, KIND_GRAM, KIND_POLY, KIND_UPDATE, KIND_APPLY, KIND_NORM = range(6)
+KIND_COUNT = 6
+KIND_NAMES = ("momentum", "gram", "poly", "update", "apply", "norm")
 
 EXPORTS = ("muon_version", "muon_workspace_size", "muon_init", "muon_step", "muon_destroy",
            "muon_last_error", "muon_describe", "muon_profile_enable", "muon_profile_read")
@@ -54,11 +54,16 @@ class MuonError(RuntimeError):
 _lib = None
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load the built library (fails loudly if it has not been built)."""
+def load(path: str = None) -> ctypes.CDLL:
+    """Load the built library (fails loudly if it has not been built).
+
+    ``MUON_LIBRARY`` in the environment selects another build of the same
+    library (for comparing build variants); the default is the in-tree build.
+    """
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("MUON_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise FileNotFoundError(f"{path} is missing: build it with `python -m muon_newton_schulz_03_amd.build`")
     lib = ctypes.CDLL(path)

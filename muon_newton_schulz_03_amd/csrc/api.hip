@@ -18,6 +18,8 @@ namespace muon {
 hipError_t launch_momentum(const MomArgs& args, int blocks, hipStream_t stream);
 hipError_t launch_apply(const ApplyArgs& args, int blocks, hipStream_t stream);
 hipError_t launch_stage(int stage, bool f32, const StageArgs& args, int blocks, hipStream_t stream);
+hipError_t prepare_stage_kernels();
+hipError_t launch_norm(const DevMat* mats, int n, hipStream_t stream);
 }  // namespace muon
 
 using namespace muon;
@@ -270,6 +272,7 @@ struct muon_plan {
   char* ws = nullptr;
   size_t ws_bytes = 0;
   std::vector<DevMat> hmat;            // host image of the current table
+  int cus = 256;                       // compute units of the device (persistent grids)
   DevMat* host_slots[kSlots] = {};     // pinned staging, one per device slot
   hipEvent_t slot_ev[kSlots] = {};
   bool slot_used[kSlots] = {};
@@ -419,6 +422,7 @@ int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts
     info->blocks[MUON_KIND_POLY] = (int32_t)(t.ns[0][kPoly].size() + t.ns[1][kPoly].size());
     info->blocks[MUON_KIND_UPDATE] = (int32_t)(t.ns[0][kUpd].size() + t.ns[1][kUpd].size());
     info->blocks[MUON_KIND_APPLY] = (int32_t)t.mom.size();
+    info->blocks[MUON_KIND_NORM] = n;
     info->x_master_iters = o.kmaster;
     info->path = o.path;
     int nf = 0;
@@ -496,6 +500,15 @@ int muon_init(const muon_matrix_desc* descs, int n, const muon_options* opts, vo
   }
   hipError_t e = hipEventCreateWithFlags(&p->last_ev, hipEventDisableTiming);
   if (e != hipSuccess) return cleanup(hip_fail(e, "hipEventCreate"));
+  e = prepare_stage_kernels();
+  if (e != hipSuccess) return cleanup(hip_fail(e, "hipFuncSetAttribute(dynamic LDS)"));
+  {
+    int dev = 0, cus = 0;
+    e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return cleanup(hip_fail(e, "hipDeviceGetAttribute(CU count)"));
+    if (cus > 0) p->cus = cus;
+  }
 
   // Tile tables: staged through pinned memory, uploaded once; init waits for
   // them so the staging can be released.
@@ -598,14 +611,20 @@ int muon_step(muon_plan* p, const muon_matrix_desc* descs, int n, float a, float
   }
   static const int kKinds[3] = {MUON_KIND_GRAM, MUON_KIND_POLY, MUON_KIND_UPDATE};
   static const char* kNames[3] = {"gram launch", "poly launch", "update launch"};
+  if (T > 0) {
+    if ((rc = prof_begin(p, MUON_KIND_NORM, stream, &pi))) return rc;
+    if ((rc = check_launch(launch_norm(mats, p->n, stream), "norm launch"))) return rc;
+    if ((rc = prof_end(p, stream, pi))) return rc;
+  }
   for (int t = 1; t <= T; ++t) {
     for (int k = 0; k < 3; ++k) {
       for (int prec = 0; prec < 2; ++prec) {
-        const int blocks = (int)p->tab.ns[prec][k].size();
-        if (!blocks) continue;
-        StageArgs sa{mats, (const Tile*)(p->ws + p->lay.ns_tiles[prec][k]), t, T, p->opt.kmaster, a, b, c, lr};
+        const int ntab = (int)p->tab.ns[prec][k].size();
+        if (!ntab) continue;
+        StageArgs sa{mats, (const Tile*)(p->ws + p->lay.ns_tiles[prec][k]), ntab, t, T, p->opt.kmaster, a, b, c, lr};
+        const int grid = ntab;
         if ((rc = prof_begin(p, kKinds[k], stream, &pi))) return rc;
-        if ((rc = check_launch(launch_stage(k + 1, prec == 1, sa, blocks, stream), kNames[k]))) return rc;
+        if ((rc = check_launch(launch_stage(k + 1, prec == 1, sa, grid, stream), kNames[k]))) return rc;
         if ((rc = prof_end(p, stream, pi))) return rc;
       }
     }

@@ -6,19 +6,27 @@
 // Nesterov momentum, then replace the update by its nearest semi-orthogonal
 // matrix via Newton-Schulz steps, then apply it to the weights.
 //
-//   momentum_kernel   M <- mu M + G (one fp32 rounding), U = G + mu M or M,
-//                     per-tile partial sums of U^2, X0 = U written in the
-//                     canonical (short side first) orientation, fp32 and/or bf16.
-//   ns_stage_kernel<1> A = s^2 X X^T     (upper tiles, mirrored store)
-//   ns_stage_kernel<2> B = b A + c A A    (A symmetric: A A = A A^T)
+//   momentum_kernel    M <- mu M + G (one fp32 rounding), U = G + mu M or M,
+//                      per-tile partial sums of U^2, X0 = U written in the
+//                      canonical (short side first) orientation.
+//   norm_kernel        s = 1 / (||U||_F + eps) per matrix.
+//   ns_stage_kernel<1> A = s^2 X X^T     (upper tiles; A stored upper-triangle only)
+//   ns_stage_kernel<2> B = b A + c A A    (A symmetric: A A = A A^T; B upper only)
 //   ns_stage_kernel<3> X <- a X + B X; on the last step W <- W - lr s O
 //   apply_kernel       T == 0: W <- W - lr s X0
 //
 // The three products share one MFMA main loop: 128x128 output tile per
-// 256-thread block, 4 waves each owning 64x64 as 2x2 v_mfma_f32_32x32x16_bf16
-// (or v_mfma_f32_32x32x2_f32 on the fp32 path), K staged through LDS in
-// 128-byte rows with an XOR swizzle, double-buffered through registers.
+// 256-thread block (2 per CU), 4 waves each owning 64x64 as 2x2
+// v_mfma_f32_32x32x16_bf16 (or v_mfma_f32_32x32x2_f32 on the fp32 path).
+// K streams in 128-byte slabs through a two-slab LDS ring filled by
+// direct-to-LDS buffer loads; lower-triangle slabs of A and B, and every slab
+// of X in B*X, are read with the transposing LDS reads of gfx950.  The
+// finished tile is staged in LDS so that every global access of the epilogue
+// is row-contiguous, and the epilogue's inputs are requested with the last
+// K slab.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "muon_internal.h"
 
@@ -185,63 +193,83 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(MomArgs args) {
 }
 
 // ------------------------------------------------------ weight step -------
+// W <- W - lr s O, split into a load and a store so the loads can be issued
+// ahead.  Canonical (i, j..j+3) is original (i, j+e), or (j+e, i) for a
+// transposed matrix (the _rows variants take original row R, columns C..C+3).
+// Out-of-range elements load 0 and are not stored.
+__device__ __forceinline__ float wget(const DevMat& d, size_t off) {
+  return d.w_bf16 ? bf2f(((const uint16_t*)d.w)[off]) : ((const float*)d.w)[off];
+}
+__device__ __forceinline__ void wput(const DevMat& d, size_t off, float v) {
+  if (d.w_bf16)
+    ((uint16_t*)d.w)[off] = f2bf(v);
+  else
+    ((float*)d.w)[off] = v;
+}
 
-template <bool W_BF16>
-__device__ __forceinline__ void weight_step4(const DevMat& d, int i, int j, const float* o, float lr_eff) {
-  // canonical (i, j..j+3) -> original (i, j+e) or (j+e, i)
-  if (i >= d.m) return;
-  if (!d.transposed) {
-    const size_t off = (size_t)i * d.cols + j;
-    if (d.vec_w && j + 3 < d.n) {
-      if (W_BF16) {
-        u32x2* p = (u32x2*)((uint16_t*)d.w + off);
-        float w[4];
-        unpack4_bf16(*p, w);
-        *p = pack4_bf16(fmaf(-lr_eff, o[0], w[0]), fmaf(-lr_eff, o[1], w[1]),
-                        fmaf(-lr_eff, o[2], w[2]), fmaf(-lr_eff, o[3], w[3]));
-      } else {
-        f32x4* p = (f32x4*)((float*)d.w + off);
-        f32x4 w = *p;
-        w.x = fmaf(-lr_eff, o[0], w.x);
-        w.y = fmaf(-lr_eff, o[1], w.y);
-        w.z = fmaf(-lr_eff, o[2], w.z);
-        w.w = fmaf(-lr_eff, o[3], w.w);
-        *p = w;
-      }
-      return;
+// original row R, columns C..C+3
+__device__ __forceinline__ void weight_load_rows(const DevMat& d, int R, int C, float* w) {
+  w[0] = w[1] = w[2] = w[3] = 0.f;
+  if (R >= d.rows) return;
+  const size_t off = (size_t)R * d.cols + C;
+  if (d.vec_w && C + 3 < d.cols) {
+    if (d.w_bf16) {
+      unpack4_bf16(*(const u32x2*)((const uint16_t*)d.w + off), w);
+    } else {
+      f32x4 x = *(const f32x4*)((const float*)d.w + off);
+      w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
     }
+    return;
+  }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (j + e >= d.n) break;
-      if (W_BF16) {
-        uint16_t* p = (uint16_t*)d.w + off + e;
-        *p = f2bf(fmaf(-lr_eff, o[e], bf2f(*p)));
-      } else {
-        float* p = (float*)d.w + off + e;
-        *p = fmaf(-lr_eff, o[e], *p);
-      }
-    }
+  for (int e = 0; e < 4; ++e)
+    if (C + e < d.cols) w[e] = wget(d, off + e);
+}
+__device__ __forceinline__ void weight_store_rows(const DevMat& d, int R, int C, const float* w) {
+  if (R >= d.rows) return;
+  const size_t off = (size_t)R * d.cols + C;
+  if (d.vec_w && C + 3 < d.cols) {
+    if (d.w_bf16)
+      *(u32x2*)((uint16_t*)d.w + off) = pack4_bf16(w[0], w[1], w[2], w[3]);
+    else
+      *(f32x4*)((float*)d.w + off) = f32x4{w[0], w[1], w[2], w[3]};
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (C + e < d.cols) wput(d, off + e, w[e]);
+}
+
+// canonical (i, j..j+3) of an untransposed matrix = original row i, columns j..j+3
+__device__ __forceinline__ void weight_load(const DevMat& d, int i, int j, float* w) {
+  if (i >= d.m) {
+    w[0] = w[1] = w[2] = w[3] = 0.f;
+    return;
+  }
+  weight_load_rows(d, i, j, w);
+}
+__device__ __forceinline__ void weight_store(const DevMat& d, int i, int j, const float* w) {
+  if (i >= d.m) return;
+  weight_store_rows(d, i, j, w);
+}
+
+// Read-modify-write form (T == 0 path): canonical (i, j..j+3).
+__device__ __forceinline__ void weight_step(const DevMat& d, int i, int j, const float* o, float lr_eff) {
+  if (!d.transposed) {
+    float w[4];
+    weight_load(d, i, j, w);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = fmaf(-lr_eff, o[e], w[e]);
+    weight_store(d, i, j, w);
   } else {
+    if (i >= d.m) return;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (j + e >= d.n) break;
       const size_t off = (size_t)(j + e) * d.cols + i;
-      if (W_BF16) {
-        uint16_t* p = (uint16_t*)d.w + off;
-        *p = f2bf(fmaf(-lr_eff, o[e], bf2f(*p)));
-      } else {
-        float* p = (float*)d.w + off;
-        *p = fmaf(-lr_eff, o[e], *p);
-      }
+      wput(d, off, fmaf(-lr_eff, o[e], wget(d, off)));
     }
   }
-}
-
-__device__ __forceinline__ void weight_step(const DevMat& d, int i, int j, const float* o, float lr_eff) {
-  if (d.w_bf16)
-    weight_step4<true>(d, i, j, o, lr_eff);
-  else
-    weight_step4<false>(d, i, j, o, lr_eff);
 }
 
 // T == 0: the update is X0 itself.  Same tiling as the momentum kernel.
@@ -275,54 +303,60 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs args) {
 
 // ------------------------------------------------ Newton-Schulz stages ----
 
-// Global -> register copy of a 128-row x 128-byte operand panel whose K runs
-// along memory rows (row r of the panel = memory row row0 + r).
-__device__ __forceinline__ void load_kc(u32x4 (&r)[4], const char* base, size_t ld_bytes, int kbyte0,
-                                        int tid) {
-  const int c = tid & 7, rr = tid >> 3;
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    r[q] = *(const u32x4*)(base + (size_t)(rr + 32 * q) * ld_bytes + kbyte0 + 16 * c);
+// Operand slabs go from HBM straight into LDS (gfx950 buffer_load_dwordx4
+// ... lds): each wave instruction moves 64 x 16 bytes into 1 KiB of
+// contiguous LDS, lane l to byte 16 l, so the LDS swizzle is applied by
+// choosing which global 16-byte chunk each lane fetches.  A buffer resource
+// per slab lives in scalar registers; an empty resource (valid == false)
+// issues the instructions without touching memory, which keeps the wait
+// counts of the pipeline static.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ void store_kc(char* lds, const u32x4 (&r)[4], int tid) {
-  const int c = tid & 7, rr = tid >> 3;
+#define MUON_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+#define MUON_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+// Workgroup barrier that is also a compiler memory barrier, without the
+// fence that would make the compiler wait for every LDS-bound load.
+#define MUON_BARRIER() asm volatile("s_barrier" ::: "memory")
+
+// K-contiguous operand slab: 128 panel rows x 128 bytes of K.  Wave w moves
+// rows 32 w .. 32 w + 31 (four 8-row instructions); row r's logical chunk c
+// lands at chunk c ^ swz(r).
+__device__ __forceinline__ void dma_kc(char* lds, const char* slab, uint32_t ld_bytes, bool valid, int w, int lane) {
+  const rsrc_t rs = make_rsrc(slab, valid ? 128u * ld_bytes : 0u);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int row = rr + 32 * q;
-    *(u32x4*)(lds + row * 128 + ((c ^ swz(row)) << 4)) = r[q];
+    const int n = 4 * w + q;
+    const int row = 8 * n + (lane >> 3);
+    const uint32_t voff = (uint32_t)row * ld_bytes + 16u * (uint32_t)((lane & 7) ^ swz(row));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MUON_LDS(lds + n * 1024), 16, voff, 0, 0, 0);
   }
 }
 
-// Panel whose K runs down memory columns: element (j, k) of the panel is
-// memory (k0 + k, j0 + j).  Each thread reads a 4(k) x 8(j) bf16 block (or
-// 4 x 4 fp32) and writes it transposed, so LDS rows are again K-contiguous.
+// Row-major X slab for the B*X product: BK rows of K (memory rows), each the
+// tile's 128 columns (256 bytes bf16 / 512 bytes fp32), copied untransposed.
+// bf16 rows are swizzled in 16-byte chunks by xswz(k) so that the transposing
+// fragment reads below are conflict-free; fp32 rows are stored plainly.
+__device__ __forceinline__ int xswz(int k) { return 4 * (k & 3); }
 template <bool F32>
-__device__ __forceinline__ void load_tr(u32x4 (&r)[4], const char* base, size_t ld_bytes, int k0, int jbyte0,
-                                        int tid) {
-  const int jg = F32 ? (tid & 31) : (tid & 15);
-  const int kg = F32 ? (tid >> 5) : (tid >> 4);
+__device__ __forceinline__ void dma_x(char* lds, const char* slab, uint32_t ld_bytes, bool valid, int w, int lane) {
+  constexpr int BK = F32 ? 32 : 64;
+  const rsrc_t rs = make_rsrc(slab, valid ? (uint32_t)BK * ld_bytes : 0u);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) r[q] = *(const u32x4*)(base + (size_t)(k0 + 4 * kg + q) * ld_bytes + jbyte0 + 16 * jg);
-}
-template <bool F32>
-__device__ __forceinline__ void store_tr(char* lds, const u32x4 (&r)[4], int tid) {
-  if (F32) {
-    const int jg = tid & 31, kg = tid >> 5;  // kg = 16-byte chunk (4 floats of K)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 4 * jg + e;
-      *(u32x4*)(lds + row * 128 + ((kg ^ swz(row)) << 4)) = u32x4{r[0][e], r[1][e], r[2][e], r[3][e]};
+  for (int q = 0; q < 4; ++q) {
+    const int n = 4 * w + q;
+    uint32_t voff;
+    if (F32) {
+      const int k = 2 * n + (lane >> 5);
+      voff = (uint32_t)k * ld_bytes + 16u * (uint32_t)(lane & 31);
+    } else {
+      const int k = 4 * n + (lane >> 4);
+      voff = (uint32_t)k * ld_bytes + 16u * (uint32_t)((lane & 15) ^ xswz(k));
     }
-  } else {
-    const int jg = tid & 15, kg = tid >> 4;  // 4 bf16 of K = half a chunk
-#pragma unroll
-    for (int dd = 0; dd < 4; ++dd) {
-      const u32x2 ev{(r[0][dd] & 0xFFFFu) | (r[1][dd] << 16), (r[2][dd] & 0xFFFFu) | (r[3][dd] << 16)};
-      const u32x2 od{(r[0][dd] >> 16) | (r[1][dd] & 0xFFFF0000u), (r[2][dd] >> 16) | (r[3][dd] & 0xFFFF0000u)};
-      const int re = 8 * jg + 2 * dd, ro = re + 1;
-      *(u32x2*)(lds + re * 128 + (((kg >> 1) ^ swz(re)) << 4) + ((kg & 1) << 3)) = ev;
-      *(u32x2*)(lds + ro * 128 + (((kg >> 1) ^ swz(ro)) << 4) + ((kg & 1) << 3)) = od;
-    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MUON_LDS(lds + n * 1024), 16, voff, 0, 0, 0);
   }
 }
 
@@ -330,44 +364,133 @@ __device__ __forceinline__ void store_tr(char* lds, const u32x4 (&r)[4], int tid
 // MFMA operand A = P fragment (MFMA row <-> output column j), operand B = Q
 // fragment (MFMA column <-> output row i): each lane then holds 4
 // consecutive output columns of one output row per 4 accumulator registers.
+// Fragments of the next 16-K step are read while the current one multiplies.
+//
+// An operand slab sits in LDS in one of two layouts.  K-contiguous: 128 rows
+// (the operand's M or N index) of 128 bytes of K, read with ds_read_b128.
+// Row-major ("X layout"): BK rows of K of 128 columns, copied untransposed
+// (the X operand of B*X, and the lower-triangle slabs of A and B, which are
+// stored upper-triangle only).  bf16 X-layout fragments take two
+// ds_read_b64_tr_b16 each: in a 16-lane group, lane r addresses K row
+// k0 + r/4, columns J0 + 4 (r % 4) .. +3, and lane i then receives K rows
+// k0..k0+3 of column J0 + i -- the MFMA operand layout (lane l: column l % 32,
+// K 8 (l / 32) .. +7).  fp32 X-layout fragments take four scalar reads.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 frag_kc(const char* l, int row, int chunk) {
+  return *(const u32x4*)(l + row * 128 + ((chunk ^ swz(row)) << 4));
+}
+__device__ __forceinline__ u32x4 frag_x32(const char* l, int col, int chunk) {
+  u32x4 f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) f[e] = *(const uint32_t*)(l + (4 * chunk + e) * 512 + 4 * col);
+  return f;
+}
+// Two bf16 X-layout fragments (columns base + 0..31 and base + 32..63) for
+// K step ks.  The four transposing reads and their wait sit in one asm
+// block: the compiler would otherwise wait for every in-flight
+// direct-to-LDS load before each of them.
+__device__ __forceinline__ void frags_x16(u32x4 (&f)[2], const char* l, int base, int lane, int ks) {
+  const int g = lane >> 4, r = lane & 15;
+  uint32_t addr[2][2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int jel = base + n * 32 + 16 * (g & 1) + 4 * (r & 3);  // first of 4 columns
+    const int cb = (jel * 2) >> 4, half = ((jel * 2) >> 3) & 1;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int k = 16 * ks + 8 * (g >> 1) + 4 * m + (r >> 2);
+      addr[n][m] = (uint32_t)(uintptr_t)(l + k * 256 + ((cb ^ xswz(k)) << 4) + (half << 3));
+    }
+  }
+  u32x2 t00, t01, t10, t11;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(t00), "=&v"(t01), "=&v"(t10), "=&v"(t11)
+      : "v"(addr[0][0]), "v"(addr[0][1]), "v"(addr[1][0]), "v"(addr[1][1])
+      : "memory");
+  f[0] = u32x4{t00.x, t00.y, t01.x, t01.y};
+  f[1] = u32x4{t10.x, t10.y, t11.x, t11.y};
+}
+
+template <bool F32, bool X>
+__device__ __forceinline__ void load_op(u32x4 (&f)[2], const char* l, int base, int lane, int ks) {
+  const int chunk = 2 * ks + (lane >> 5);
+  if (!X) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) f[n] = frag_kc(l, base + n * 32 + (lane & 31), chunk);
+  } else if (F32) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) f[n] = frag_x32(l, base + n * 32 + (lane & 31), chunk);
+  } else {
+    frags_x16(f, l, base, lane, ks);
+  }
+}
+
+template <bool F32, bool Q_X, bool P_X>
+__device__ __forceinline__ void load_frags(u32x4 (&qf)[2], u32x4 (&pf)[2], const char* lq, const char* lp, int wm,
+                                           int wn, int lane, int ks) {
+  load_op<F32, Q_X>(qf, lq, wm * 64, lane, ks);
+  load_op<F32, P_X>(pf, lp, wn * 64, lane, ks);
+}
+
 template <bool F32>
-__device__ __forceinline__ void mma_slab(f32x16 (&acc)[2][2], const char* lq, const char* lp, int wm, int wn,
-                                         int lane) {
+__device__ __forceinline__ void mma_frags(f32x16 (&acc)[2][2], const u32x4 (&qf)[2], const u32x4 (&pf)[2]) {
+  if (!F32) {
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const int chunk = 2 * ks + (lane >> 5);
-    u32x4 qf[2], pf[2];
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      const int row = wm * 64 + mi * 32 + (lane & 31);
-      qf[mi] = *(const u32x4*)(lq + row * 128 + ((chunk ^ swz(row)) << 4));
-    }
+      for (int nj = 0; nj < 2; ++nj)
+        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pf[nj]),
+                                                               __builtin_bit_cast(bf16x8, qf[mi]), acc[mi][nj], 0,
+                                                               0, 0);
+  } else {
+    // Four fp32 K values per lane: MFMA e takes element e; both operands use
+    // the same K order, so the contraction covers all 32 K of the slab.
 #pragma unroll
-    for (int nj = 0; nj < 2; ++nj) {
-      const int row = wn * 64 + nj * 32 + (lane & 31);
-      pf[nj] = *(const u32x4*)(lp + row * 128 + ((chunk ^ swz(row)) << 4));
-    }
-    if (!F32) {
+    for (int e = 0; e < 4; ++e)
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
         for (int nj = 0; nj < 2; ++nj)
-          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pf[nj]),
-                                                                 __builtin_bit_cast(bf16x8, qf[mi]),
-                                                                 acc[mi][nj], 0, 0, 0);
-    } else {
-      // Four fp32 K values per lane: MFMA e takes element e; both operands use
-      // the same K order, so the contraction covers all 32 K of the slab.
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-          for (int nj = 0; nj < 2; ++nj)
-            acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(pf[nj][e]),
-                                                                __uint_as_float(qf[mi][e]), acc[mi][nj], 0, 0, 0);
-    }
+          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(pf[nj][e]), __uint_as_float(qf[mi][e]),
+                                                              acc[mi][nj], 0, 0, 0);
   }
+}
+
+template <bool F32, bool Q_X, bool P_X>
+__device__ __forceinline__ void mma_slab(f32x16 (&acc)[2][2], const char* lq, const char* lp, int wm, int wn,
+                                         int lane) {
+  u32x4 qa[2], pa[2], qb[2], pb[2];
+  load_frags<F32, Q_X, P_X>(qa, pa, lq, lp, wm, wn, lane, 0);
+  load_frags<F32, Q_X, P_X>(qb, pb, lq, lp, wm, wn, lane, 1);
+  mma_frags<F32>(acc, qa, pa);
+  load_frags<F32, Q_X, P_X>(qa, pa, lq, lp, wm, wn, lane, 2);
+  mma_frags<F32>(acc, qb, pb);
+  load_frags<F32, Q_X, P_X>(qb, pb, lq, lp, wm, wn, lane, 3);
+  mma_frags<F32>(acc, qa, pa);
+  mma_frags<F32>(acc, qb, pb);
+}
+
+// ---- epilogue helpers.  The finished 128x128 tile is staged in LDS as fp32,
+// 16-byte chunk (i, jc) of row i stored at chunk jc ^ cswz(i).  With this
+// swizzle every epilogue access is a conflict-free 16-byte LDS access: the
+// MFMA-layout writes (16 consecutive rows, one chunk), row reads (one row,
+// 16 consecutive chunks) and 4x4-block reads (rows 4L+e, L = 0..15, one chunk).
+__device__ __forceinline__ int cswz(int i) { return (i ^ (i >> 2)) & 15; }
+__device__ __forceinline__ float* cptr(float* ct, int i, int j) { return ct + i * kTile + (((j >> 2) ^ cswz(i)) << 2); }
+__device__ __forceinline__ void crow(const float* ct, int r, int c, float* v) {
+  f32x4 x = *(const f32x4*)cptr(const_cast<float*>(ct), r, c);
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+}
+// blk[e][f] = C[c + e][r + f]: a 4x4 block read as four row chunks.
+__device__ __forceinline__ void cblock(const float* ct, int c, int r, float (&blk)[4][4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) crow(ct, c + e, r, blk[e]);
 }
 
 template <bool F32>
@@ -386,78 +509,343 @@ __device__ __forceinline__ void load4(const void* base, size_t off, float* v) {
     unpack4_bf16(*(const u32x2*)((const uint16_t*)base + off), v);
   }
 }
-template <bool F32>
-__device__ __forceinline__ void store1(void* base, size_t off, float v) {
-  if (F32)
-    ((float*)base)[off] = v;
-  else
-    ((uint16_t*)base)[off] = f2bf(v);
+
+// LDS of a product block: two K slabs of the Q and P operands (32 KiB
+// each).  While one slab is multiplied the next is in flight into the other;
+// after the last slab both hold the staged 128x128 fp32 output tile.
+constexpr int kSlabLds = 2 * kTile * 128;
+constexpr int kStageLds = 2 * kSlabLds;
+constexpr int kBlocksPerCu = 2;
+
+// LDS-only workgroup barrier: waits for this wave's LDS operations, not for
+// its in-flight direct-to-LDS loads or global stores.
+#define MUON_LDS_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+
+// One block per matrix: s = 1 / (||U||_F + eps) from the momentum kernel's
+// per-tile partial sums (fixed summation order: deterministic).
+__global__ __launch_bounds__(kThreads) void norm_kernel(const DevMat* mats) {
+  const DevMat& d = mats[blockIdx.x];
+  __shared__ double scratch[kThreads];
+  double nu;
+  const float inv = block_inv_norm(d, scratch, &nu);
+  if (threadIdx.x == 0) {
+    d.sc[0] = inv;
+    d.sc[1] = (float)nu;
+  }
 }
 
-// Symmetric store of a 4-column strip: row i, columns j..j+3 and the mirror.
-// Diagonal tiles keep only i <= j' so both triangles hold the same values.
+// Where a tile's operand panels are, and its K extent (wave-uniform).  A
+// symmetric operand (A or B) is stored upper-triangle only: row panel `pt`'s
+// K slab at tile column tk < pt is read from the stored tile (tk, pt) in the
+// X layout.  X itself (the P operand of B*X) is always read in the X layout.
+struct TileOps {
+  const char* q;   // Q matrix base (row panel i0: row-major, ld qld)
+  const char* p;   // P matrix base
+  uint32_t qld, pld;
+  int qt, pt;      // panel tile indices of Q and P (symmetric operands)
+  int nk;
+  int i0, j0;
+  int mat;
+  bool diag;
+};
+
+template <int STAGE, bool F32>
+__device__ __forceinline__ TileOps tile_ops(const StageArgs& args, const Tile& tl) {
+  constexpr int ES = F32 ? 4 : 2;
+  const DevMat& d = args.mats[tl.mat];
+  TileOps o;
+  o.mat = tl.mat;
+  o.i0 = tl.ti * kTile;
+  o.j0 = tl.tj * kTile;
+  o.qt = tl.ti;
+  o.pt = tl.tj;
+  o.diag = tl.ti == tl.tj;
+  const char* xin = (const char*)d.xo[(args.t - 1) & 1];
+  int K;
+  if (STAGE == 1) {  // A = X X^T: both panels are row panels of X, K = np
+    o.qld = o.pld = (uint32_t)d.np * ES;
+    o.q = o.p = xin;
+    K = d.np;
+  } else if (STAGE == 2) {  // A A^T: row panels of the upper-stored A, K = mp
+    o.qld = o.pld = (uint32_t)d.mp * ES;
+    o.q = o.p = (const char*)d.a;
+    K = d.mp;
+  } else {  // B X: row panel of the upper-stored B, column panel of X, K = mp
+    o.qld = (uint32_t)d.mp * ES;
+    o.q = (const char*)d.b;
+    o.pld = (uint32_t)d.np * ES;
+    o.p = xin;
+    K = d.mp;
+  }
+  o.nk = K / (128 / ES);
+  return o;
+}
+
+// Request K slab kt of one operand into `lds`.  `sym`: the operand is stored
+// upper-triangle only (returns true when the slab lands in the X layout).
 template <bool F32>
-__device__ __forceinline__ void store_sym(void* out, int ld, int i, int j, const float* v, bool diag) {
-  if (!diag) {
-    store4<F32>(out, (size_t)i * ld + j, v);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) store1<F32>(out, (size_t)(j + e) * ld + i, v[e]);
-  } else {
+__device__ __forceinline__ bool dma_operand(char* lds, const char* base, uint32_t ld, int panel, bool sym,
+                                            bool xlayout, int kt, int w, int lane) {
+  constexpr int ES = F32 ? 4 : 2;
+  constexpr int BK = 128 / ES;
+  const int k0 = kt * BK;  // first K element of the slab
+  if (xlayout || (sym && k0 < panel * kTile)) {
+    // memory rows k0.., columns panel*128.. (X itself, or the stored tile (tk, panel))
+    dma_x<F32>(lds, base + (size_t)k0 * ld + (size_t)panel * kTile * ES, ld, true, w, lane);
+    return true;
+  }
+  dma_kc(lds, base + (size_t)panel * kTile * ld + (size_t)k0 * ES, ld, true, w, lane);
+  return false;
+}
+
+// Writes of the 4 columns c..c+3 of a diagonal tile's row r: only the upper
+// triangle (r <= column) comes from the direct pass.
+template <bool F32>
+__device__ __forceinline__ void store4_upper(void* out, size_t off, const float* v, int r, int c) {
+  if (r <= c) {
+    store4<F32>(out, off, v);
+  } else if (r <= c + 3) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (i <= j + e) {
-        store1<F32>(out, (size_t)i * ld + j + e, v[e]);
-        store1<F32>(out, (size_t)(j + e) * ld + i, v[e]);
+      if (r <= c + e) {
+        if (F32)
+          ((float*)out)[off + e] = v[e];
+        else
+          ((uint16_t*)out)[off + e] = f2bf(v[e]);
+      }
+  }
+}
+// ... and the strictly lower triangle (row R > column cc + e) from the mirror pass.
+template <bool F32>
+__device__ __forceinline__ void store4_lower(void* out, size_t off, const float* v, int R, int cc) {
+  if (R > cc + 3) {
+    store4<F32>(out, off, v);
+  } else if (R > cc) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (R > cc + e) {
+        if (F32)
+          ((float*)out)[off + e] = v[e];
+        else
+          ((uint16_t*)out)[off + e] = f2bf(v[e]);
       }
   }
 }
 
-template <int STAGE, bool F32>
-__global__ __launch_bounds__(kThreads, 2) void ns_stage_kernel(StageArgs args) {
-  constexpr int ES = F32 ? 4 : 2;
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * kTile * 128];
+// Inputs of a tile's epilogue, prefetched while its last K slab multiplies
+// (bf16 products): A at the direct and mirror positions (stage 2), the
+// master X (stage 3; fp32 copy or bf16).  Global stores share the in-order
+// vector-memory counter with loads, so every load of the epilogue is issued
+// before its first store.  Row pass: thread handles tile rows (tid >> 5) + 8 q
+// and columns c..c+3; column pass: the 4x4 block C[c..c+3][r..r+3] with
+// r = 4 (tid >> 5) + 32 q, written as 4 rows of the transposed tile.
+// Stage 3 kernels come in variants: kMaster32 (the a*X term reads the fp32
+// copy of X) and kLast (last iteration: the weight step instead of storing X).
+constexpr int kMaster32 = 1, kLast = 2;
 
+struct EpiIn {
+  u32x2 dir16[16];  // bf16 at the direct positions (A of stage 2, master X of stage 3)
+  f32x4 dir32[16];  // fp32 master X (stage 3, kMaster32)
+};
+
+template <int STAGE, bool F32, int MODE>
+__device__ __forceinline__ void epi_prefetch(const StageArgs& args, const DevMat& d, const TileOps& o, EpiIn& in,
+                                             int tid) {
+  if (F32) return;  // the fp32 path loads as it goes
+  const int c = 4 * (tid & 31), rbase = tid >> 5;
+  if (STAGE == 2) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      in.dir16[q] = *(const u32x2*)((const uint16_t*)d.a + (size_t)(o.i0 + rbase + 8 * q) * d.mp + o.j0 + c);
+  } else if (STAGE == 3) {
+    const void* xin = d.xo[(args.t - 1) & 1];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const size_t off = (size_t)(o.i0 + rbase + 8 * q) * d.np + o.j0 + c;
+      if (MODE & kMaster32)
+        in.dir32[q] = *(const f32x4*)(d.x32 + off);
+      else
+        in.dir16[q] = *(const u32x2*)((const uint16_t*)xin + off);
+    }
+  }
+}
+
+template <int STAGE, bool F32, int MODE>
+__device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMat& d, const TileOps& o,
+                                              const f32x16 (&acc)[2][2], const EpiIn& in, float* ct, int tid, int lane,
+                                              int wm, int wn) {
+  const int t = args.t;
+  const int c = 4 * (tid & 31), rbase = tid >> 5;
+  const int i0 = o.i0, j0 = o.j0;
+
+  float pre = 1.f;  // stage 1 of the first iteration works on U: A = s^2 U U^T
+  if (STAGE == 1 && t == 1) pre = d.sc[0] * d.sc[0];
+  float alpha = args.a, beta = 1.f;
+  if (STAGE == 3 && t == 1) {
+    alpha = args.a * d.sc[0];
+    beta = d.sc[0];
+  }
+  constexpr bool last = STAGE == 3 && (MODE & kLast);
+  constexpr bool master32 = STAGE == 3 && !F32 && (MODE & kMaster32);
+  const bool write32 = STAGE == 3 && !F32 && !last && t < args.kmaster;
+  const float lr_eff = args.lr * d.scale;
+  const void* xin = d.xo[(t - 1) & 1];
+  void* xout = d.xo[t & 1];
+  void* sym_out = STAGE == 1 ? d.a : d.b;
+
+  // ---- stage the tile in LDS (all of it: both K slabs are free now)
+  {
+    const int h = lane >> 5;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      const int i = wm * 64 + mi * 32 + (lane & 31);
+#pragma unroll
+      for (int nj = 0; nj < 2; ++nj)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(f32x4*)cptr(ct, i, wn * 64 + nj * 32 + 8 * g + 4 * h) =
+              f32x4{acc[mi][nj][4 * g], acc[mi][nj][4 * g + 1], acc[mi][nj][4 * g + 2], acc[mi][nj][4 * g + 3]};
+    }
+  }
+  MUON_LDS_BARRIER();
+
+  auto in_dir = [&](int q, float* v) {  // epilogue input at the direct position of row pass q
+    if (F32) {
+      const size_t off = STAGE == 2 ? (size_t)(i0 + rbase + 8 * q) * d.mp + j0 + c
+                                    : (size_t)(i0 + rbase + 8 * q) * d.np + j0 + c;
+      load4<true>(STAGE == 2 ? (const void*)d.a : xin, off, v);
+    } else if (master32) {
+      v[0] = in.dir32[q].x; v[1] = in.dir32[q].y; v[2] = in.dir32[q].z; v[3] = in.dir32[q].w;
+    } else {
+      unpack4_bf16(in.dir16[q], v);
+    }
+  };
+
+  if (STAGE == 1 || STAGE == 2) {
+    // A and B are stored upper-triangle only: an off-diagonal tile writes
+    // itself, a diagonal tile also its strictly lower triangle (below).
+    // direct tile (i, j)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int r = rbase + 8 * q;
+      float v[4];
+      crow(ct, r, c, v);
+      if (STAGE == 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] *= pre;
+      } else {
+        float av[4];
+        in_dir(q, av);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = fmaf(args.c, v[e], args.b * av[e]);
+      }
+      const size_t off = (size_t)(i0 + r) * d.mp + j0 + c;
+      if (o.diag)
+        store4_upper<F32>(sym_out, off, v, r, c);
+      else
+        store4<F32>(sym_out, off, v);
+    }
+    // lower triangle of a diagonal tile: row i0 + R, columns i0 + c.. hold C[c..c+3][R]
+    if (o.diag) {
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) {
+        const int r = 4 * rbase + 32 * qb;
+        float blk[4][4];
+        cblock(ct, c, r, blk);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          float w[4];
+          const size_t off = (size_t)(j0 + r + f) * d.mp + i0 + c;
+          if (STAGE == 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = blk[e][f] * pre;
+          } else {
+            float av[4];
+            load4<F32>(d.a, off, av);  // A is symmetric: the lower value equals the stored upper one
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = fmaf(args.c, blk[e][f], args.b * av[e]);
+          }
+          store4_lower<F32>(sym_out, off, w, r + f, c);
+        }
+      }
+    }
+  } else {
+    float wrow[16][4];
+    if (last && !d.transposed) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) weight_load(d, i0 + rbase + 8 * q, j0 + c, wrow[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int r = rbase + 8 * q;
+      const size_t off = (size_t)(i0 + r) * d.np + j0 + c;
+      float v[4], xv[4];
+      crow(ct, r, c, v);
+      in_dir(q, xv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = fmaf(alpha, xv[e], beta * v[e]);
+      if (!last) {
+        store4<F32>(xout, off, v);
+        if (write32) *(f32x4*)(d.x32 + off) = f32x4{v[0], v[1], v[2], v[3]};
+      } else if (!d.transposed) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = fmaf(-lr_eff, v[e], wrow[q][e]);
+        weight_store(d, i0 + r, j0 + c, v);
+      } else {
+        *(f32x4*)cptr(ct, r, c) = f32x4{v[0], v[1], v[2], v[3]};  // O back into the staged tile
+      }
+    }
+    if (last && d.transposed && j0 < d.n) {
+      // W is the transpose of the canonical X: W row (j0 + R) holds O[i0 + c..][j0 + R]
+      float wv[16][4];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) weight_load_rows(d, j0 + 4 * rbase + 32 * (q >> 2) + (q & 3), i0 + c, wv[q]);
+      MUON_LDS_BARRIER();
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) {
+        const int r = 4 * rbase + 32 * qb;
+        float blk[4][4];
+        cblock(ct, c, r, blk);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          float w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = fmaf(-lr_eff, blk[e][f], wv[4 * qb + f][e]);
+          weight_store_rows(d, j0 + r + f, i0 + c, w);
+        }
+      }
+    } else if (last && d.transposed) {
+      MUON_LDS_BARRIER();  // keep the barrier count uniform across the block
+    }
+  }
+}
+
+// One output tile per block.  K slabs stream into a two-slab LDS ring with
+// direct-to-LDS loads: slab kt + 1 is requested right after the barrier that
+// opens slab kt.  The tile's epilogue inputs are requested with the last slab.
+template <int STAGE, bool F32, int MODE>
+__global__ __launch_bounds__(kThreads, kBlocksPerCu) void ns_stage_kernel(StageArgs args) {
+  constexpr int ES = F32 ? 4 : 2;
+  constexpr int BK = 128 / ES;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
   const Tile tl = args.tiles[blockIdx.x];
   if (tl.mat == kNullMat) return;
   const DevMat& d = args.mats[tl.mat];
+  const TileOps o = tile_ops<STAGE, F32>(args, tl);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int i0 = tl.ti * kTile, j0 = tl.tj * kTile;
-  const int t = args.t;
-  const char* xin = (const char*)d.xo[(t - 1) & 1];
+  const int w = __builtin_amdgcn_readfirstlane(wave);
 
-  const char* qbase;
-  const char* pbase;
-  size_t q_ld, p_ld;
-  int K;
-  if (STAGE == 1) {
-    q_ld = p_ld = (size_t)d.np * ES;
-    qbase = xin + (size_t)i0 * q_ld;
-    pbase = xin + (size_t)j0 * p_ld;
-    K = d.np;
-  } else if (STAGE == 2) {
-    q_ld = p_ld = (size_t)d.mp * ES;
-    qbase = (const char*)d.a + (size_t)i0 * q_ld;
-    pbase = (const char*)d.a + (size_t)j0 * p_ld;
-    K = d.mp;
-  } else {
-    q_ld = (size_t)d.mp * ES;
-    qbase = (const char*)d.b + (size_t)i0 * q_ld;
-    p_ld = (size_t)d.np * ES;
-    pbase = xin;
-    K = d.mp;
-  }
-
-  float pre = 1.f;  // stage 1 of the first iteration: A = s^2 U U^T
-  if (STAGE == 1 && t == 1) {
-    double nu;
-    const float inv = block_inv_norm(d, (double*)smem, &nu);
-    pre = inv * inv;
-    if (tl.ti == 0 && tl.tj == 0 && tid == 0) {
-      d.sc[0] = inv;
-      d.sc[1] = (float)nu;
-    }
-  }
+  // K slabs below the diagonal of a symmetric operand come first in K order
+  // (k < panel * 128), so the loop runs in phases of fixed slab layouts: Q in
+  // the X layout for k < qt * 128, P for k < pt * 128 (stage 2, qt <= pt) or
+  // always (stage 3, X itself).
+  constexpr bool kSymQ = STAGE >= 2, kSymP = STAGE == 2;
+  auto issue = [&](int kt) {
+    char* lq = smem + (kt & 1) * kSlabLds;
+    dma_operand<F32>(lq, o.q, o.qld, o.qt, kSymQ, false, kt, w, lane);
+    dma_operand<F32>(lq + kTile * 128, o.p, o.pld, o.pt, kSymP, STAGE == 3, kt, w, lane);
+  };
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -467,108 +855,58 @@ __global__ __launch_bounds__(kThreads, 2) void ns_stage_kernel(StageArgs args) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][nj][v] = 0.f;
 
-  constexpr int BK = 128 / ES;  // K elements per 128-byte slab
-  const int nk = K / BK;
-  u32x4 rq[4], rp[4];
-  load_kc(rq, qbase, q_ld, 0, tid);
-  if (STAGE == 3)
-    load_tr<F32>(rp, pbase, p_ld, 0, j0 * ES, tid);
-  else
-    load_kc(rp, pbase, p_ld, 0, tid);
-  store_kc(smem, rq, tid);
-  if (STAGE == 3)
-    store_tr<F32>(smem + kTile * 128, rp, tid);
-  else
-    store_kc(smem + kTile * 128, rp, tid);
-  __syncthreads();
+  // All slabs but the last run in the phases; the last slab (always in the
+  // upper triangle: K-contiguous Q, and P too unless it is X) also requests
+  // the epilogue's inputs.
+  auto phase = [&](auto qx, auto px, int kb, int ke) {
+    for (int kt = kb; kt < ke; ++kt) {
+      MUON_WAIT_VMCNT(0);  // this wave's part of slab kt has landed ...
+      MUON_LDS_BARRIER();  // ... everyone's, and slab kt - 1 is no longer read
+      issue(kt + 1);
+      const char* lq = smem + (kt & 1) * kSlabLds;
+      mma_slab<F32, decltype(qx)::value, decltype(px)::value>(acc, lq, lq + kTile * 128, wm, wn, lane);
+    }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  constexpr int kSlabsPerTile = kTile / BK;
+  const int nlast = o.nk - 1;
+  issue(0);
+  if (STAGE == 1) {
+    phase(F_{}, F_{}, 0, nlast);
+  } else if (STAGE == 2) {
+    const int kq = o.qt * kSlabsPerTile, kp = o.pt * kSlabsPerTile;
+    phase(T_{}, T_{}, 0, kq);
+    phase(F_{}, T_{}, kq, kp);
+    phase(F_{}, F_{}, kp, nlast);
+  } else {
+    const int kq = o.qt * kSlabsPerTile;
+    phase(T_{}, T_{}, 0, kq);
+    phase(F_{}, T_{}, kq, nlast);
+  }
+  EpiIn in;
+  {
+    MUON_WAIT_VMCNT(0);
+    MUON_LDS_BARRIER();
+    epi_prefetch<STAGE, F32, MODE>(args, d, o, in, tid);
+    const char* lq = smem + (nlast & 1) * kSlabLds;
+    mma_slab<F32, false, STAGE == 3>(acc, lq, lq + kTile * 128, wm, wn, lane);
+  }
+  MUON_LDS_BARRIER();  // the last slab has been read by all: LDS holds the staged tile next
+  tile_epilogue<STAGE, F32, MODE>(args, d, o, acc, in, (float*)smem, tid, lane, wm, wn);
+}
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      load_kc(rq, qbase, q_ld, (kt + 1) * 128, tid);
-      if (STAGE == 3)
-        load_tr<F32>(rp, pbase, p_ld, (kt + 1) * BK, j0 * ES, tid);
-      else
-        load_kc(rp, pbase, p_ld, (kt + 1) * 128, tid);
-    }
-    const char* lq = smem + buf * (2 * kTile * 128);
-    mma_slab<F32>(acc, lq, lq + kTile * 128, wm, wn, lane);
-    if (more) {
-      char* nq = smem + (buf ^ 1) * (2 * kTile * 128);
-      store_kc(nq, rq, tid);
-      if (STAGE == 3)
-        store_tr<F32>(nq + kTile * 128, rp, tid);
-      else
-        store_kc(nq + kTile * 128, rp, tid);
-    }
-    __syncthreads();
-  }
-
-  // ---- epilogue: lane holds output row i, columns j..j+3 per 4 registers.
-  const int h = lane >> 5;
-  const bool diag = tl.ti == tl.tj;
-  float alpha = args.a, beta = 1.f, lr_eff = 0.f;
-  bool last = false, master32 = false, write32 = false;
-  const void* xm = xin;
-  if (STAGE == 3) {
-    if (t == 1) {
-      const float inv = d.sc[0];
-      alpha = args.a * inv;
-      beta = inv;
-    }
-    last = t == args.T;
-    master32 = !F32 && t <= args.kmaster;
-    write32 = !F32 && !last && t < args.kmaster;
-    lr_eff = args.lr * d.scale;
-  }
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-    const int i = i0 + wm * 64 + mi * 32 + (lane & 31);
-#pragma unroll
-    for (int nj = 0; nj < 2; ++nj) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int j = j0 + wn * 64 + nj * 32 + 8 * g + 4 * h;
-        float v[4] = {acc[mi][nj][4 * g], acc[mi][nj][4 * g + 1], acc[mi][nj][4 * g + 2], acc[mi][nj][4 * g + 3]};
-        if (STAGE == 1) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] *= pre;
-          store_sym<F32>(d.a, d.mp, i, j, v, diag);
-        } else if (STAGE == 2) {
-          float av[4];
-          load4<F32>(d.a, (size_t)i * d.mp + j, av);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = fmaf(args.c, v[e], args.b * av[e]);
-          store_sym<F32>(d.b, d.mp, i, j, v, diag);
-        } else {
-          const size_t off = (size_t)i * d.np + j;
-          float xv[4];
-          if (master32) {
-            f32x4 x = *(const f32x4*)(d.x32 + off);
-            xv[0] = x.x; xv[1] = x.y; xv[2] = x.z; xv[3] = x.w;
-          } else {
-            load4<F32>(xm, off, xv);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = fmaf(alpha, xv[e], beta * v[e]);
-          if (!last) {
-            store4<F32>(d.xo[t & 1], off, v);
-            if (write32) *(f32x4*)(d.x32 + off) = f32x4{v[0], v[1], v[2], v[3]};
-          } else {
-            weight_step(d, i, j, v, lr_eff);
-          }
-        }
-      }
-    }
-  }
+hipError_t launch_norm(const DevMat* mats, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(norm_kernel, dim3(n), dim3(kThreads), 0, stream, mats);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------ launchers --
 
-#define MUON_STAGE_LAUNCH(S, F)                                                              \
-  hipLaunchKernelGGL((ns_stage_kernel<S, F>), dim3(blocks), dim3(kThreads), 0, stream, args); \
-  break;
+#define MUON_STAGE_KERNEL(S, F, M) ((const void*)ns_stage_kernel<S, F, M>)
+#define MUON_STAGE_LAUNCH(S, F, M)                                                                       \
+  hipLaunchKernelGGL((ns_stage_kernel<S, F, M>), dim3(blocks), dim3(kThreads), kStageLds, stream, args); \
+  return hipGetLastError();
 
 hipError_t launch_momentum(const MomArgs& args, int blocks, hipStream_t stream) {
   hipLaunchKernelGGL(momentum_kernel, dim3(blocks), dim3(kThreads), 0, stream, args);
@@ -580,17 +918,44 @@ hipError_t launch_apply(const ApplyArgs& args, int blocks, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_stage(int stage, bool f32, const StageArgs& args, int blocks, hipStream_t stream) {
-  switch (stage * 2 + (f32 ? 1 : 0)) {
-    case 2: MUON_STAGE_LAUNCH(1, false)
-    case 3: MUON_STAGE_LAUNCH(1, true)
-    case 4: MUON_STAGE_LAUNCH(2, false)
-    case 5: MUON_STAGE_LAUNCH(2, true)
-    case 6: MUON_STAGE_LAUNCH(3, false)
-    case 7: MUON_STAGE_LAUNCH(3, true)
-    default: return hipErrorInvalidValue;
+// The product kernels use more than the default 64 KiB of dynamic LDS.
+hipError_t prepare_stage_kernels() {
+  const void* fns[] = {MUON_STAGE_KERNEL(1, false, 0), MUON_STAGE_KERNEL(1, true, 0),
+                       MUON_STAGE_KERNEL(2, false, 0), MUON_STAGE_KERNEL(2, true, 0),
+                       MUON_STAGE_KERNEL(3, false, 0), MUON_STAGE_KERNEL(3, false, 1),
+                       MUON_STAGE_KERNEL(3, false, 2), MUON_STAGE_KERNEL(3, false, 3),
+                       MUON_STAGE_KERNEL(3, true, 0),  MUON_STAGE_KERNEL(3, true, 2)};
+  for (const void* f : fns) {
+    hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kStageLds);
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
+}
+
+hipError_t launch_stage(int stage, bool f32, const StageArgs& args, int blocks, hipStream_t stream) {
+  const bool last = args.t == args.T;
+  const bool m32 = !f32 && args.t <= args.kmaster;
+  if (stage == 1) {
+    if (f32) { MUON_STAGE_LAUNCH(1, true, 0) }
+    MUON_STAGE_LAUNCH(1, false, 0)
+  }
+  if (stage == 2) {
+    if (f32) { MUON_STAGE_LAUNCH(2, true, 0) }
+    MUON_STAGE_LAUNCH(2, false, 0)
+  }
+  if (stage == 3) {
+    if (f32) {
+      if (last) { MUON_STAGE_LAUNCH(3, true, 2) }
+      MUON_STAGE_LAUNCH(3, true, 0)
+    }
+    if (last) {
+      if (m32) { MUON_STAGE_LAUNCH(3, false, 3) }
+      MUON_STAGE_LAUNCH(3, false, 2)
+    }
+    if (m32) { MUON_STAGE_LAUNCH(3, false, 1) }
+    MUON_STAGE_LAUNCH(3, false, 0)
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace muon

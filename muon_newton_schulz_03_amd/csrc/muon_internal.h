@@ -61,6 +61,7 @@ struct Tile {
 struct StageArgs {
   const DevMat* mats;
   const Tile* tiles;
+  int32_t ntiles;   // table length (persistent blocks stride through it)
   int32_t t;        // iteration, 1-based
   int32_t T;        // iterations this step
   int32_t kmaster;  // bf16 path: iterations 1..kmaster read the fp32 master in a*X
