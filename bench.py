@@ -12,7 +12,6 @@ buffers).  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -25,16 +24,12 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "gpt2_small"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = [os.path.join(ROOT, "muon_newton_schulz_03_amd", "csrc", f)
-                  for f in ("kernels.hip", "muon_internal.h")]
 
 
 def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    from muon_newton_schulz_03_amd.rocprof_summary import kernel_source_hash as h
+
+    return h()
 
 
 def work_model(shapes, T):
@@ -56,8 +51,9 @@ def momentum_bytes(shapes, master: bool):
 
 
 def read_traffic(kind: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if still current."""
-    path = os.path.join(PROFILES, f"{kind}_{WORKLOAD}_traffic.txt")
+    """HBM bytes per launch of one kernel kind from the committed rocprofv3 counter
+    summary; None when there is none or the kernels changed since it was taken."""
+    path = os.path.join(PROFILES, f"{WORKLOAD}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -69,7 +65,7 @@ def read_traffic(kind: str):
     if vals.get("kernel_source_hash") != kernel_source_hash():
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals[f"{kind}_hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -115,6 +111,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--x-master-iters", type=int, default=-1)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain 256 MiB device copy first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the Muon step here has no multi-GPU path "
@@ -134,6 +132,12 @@ def main():
     grads = [inputs.gradients(WORKLOAD, t, device=dev) for t in range(total)]
     W = inputs.weights(wl.shapes, seed=11, device=dev)
     M = [torch.zeros(s, dtype=torch.float32, device=dev) for s in wl.shapes]
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     plan = MuonStep(W, grads[0], M, x_master_iters=args.x_master_iters)
     kw = dict(a=wl.coeffs[0], b=wl.coeffs[1], c=wl.coeffs[2], T=wl.T, momentum=wl.momentum,
               nesterov=wl.nesterov, lr=wl.lr)

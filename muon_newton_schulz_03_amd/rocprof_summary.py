@@ -1,0 +1,152 @@
+"""Summaries of rocprofv3 output for the Muon kernels (text files for ``profiles/``).
+
+Two summaries:
+
+* kernel statistics from ``rocprofv3 --kernel-trace --stats --output-format csv``
+  (``*_kernel_stats.csv`` and ``*_kernel_trace.csv``): per-kernel calls and
+  average durations, plus the per-dispatch durations of the product kernels;
+* HBM traffic from two ``--pmc`` runs (``FETCH_SIZE``, then ``WRITE_SIZE``,
+  KiB per dispatch) of ``bench.py --calibrate-copy``, scaled by what the same
+  counters read for the plain copy kernel of known size that run contains.
+
+    python -m muon_newton_schulz_03_amd.rocprof_summary stats  <trace_dir> <out.txt> "<command>"
+    python -m muon_newton_schulz_03_amd.rocprof_summary traffic <fetch_dir> <write_dir> <out.txt> "<commands>"
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import os
+import sys
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kernels.hip", "muon_internal.h")]
+COPY_BYTES = 256 << 20  # bench.py --calibrate-copy: one plain copy of 256 MiB
+
+KINDS = {
+    "momentum_kernel": "momentum",
+    "norm_kernel": "norm",
+    "ns_stage_kernel<1": "gram",
+    "ns_stage_kernel<2": "poly",
+    "ns_stage_kernel<3": "update",
+    "apply_kernel": "apply",
+}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kind_of(name: str):
+    for key, kind in KINDS.items():
+        if key in name:
+            return kind
+    return None
+
+
+def _one(pattern: str) -> str:
+    hits = glob.glob(pattern, recursive=True)
+    if not hits:
+        raise FileNotFoundError(pattern)
+    return hits[0]
+
+
+def stats_summary(trace_dir: str, command: str) -> str:
+    stats = list(csv.DictReader(open(_one(os.path.join(trace_dir, "**", "*kernel_stats.csv")))))
+    trace = list(csv.DictReader(open(_one(os.path.join(trace_dir, "**", "*kernel_trace.csv")))))
+    lines = ["# rocprofv3 kernel statistics, Muon step on the GPT-2 small hidden set (72 matrices, T = 5)",
+             f"# command: {command}",
+             f"# kernel source hash: {kernel_source_hash()}",
+             "# kind        calls   avg_us    min_us    max_us   kernel"]
+    agg = defaultdict(lambda: [0, 0.0, float("inf"), 0.0, ""])
+    for r in stats:
+        k = kind_of(r["Name"])
+        if not k:
+            continue
+        a = agg[(k, r["Name"])]
+        calls = int(r["Calls"])
+        a[0] += calls
+        a[1] += float(r["TotalDurationNs"]) / 1000.0
+        a[2] = min(a[2], float(r["MinNs"]) / 1000.0)
+        a[3] = max(a[3], float(r["MaxNs"]) / 1000.0)
+        a[4] = r["Name"]
+    for (k, name), (calls, tot, mn, mx, _) in sorted(agg.items()):
+        lines.append(f"{k:10s} {calls:7d} {tot / calls:9.1f} {mn:9.1f} {mx:9.1f}   {name[:70]}")
+    lines.append("# per-dispatch durations (us) of the last step, in launch order")
+    mu = [r for r in trace if kind_of(r["Kernel_Name"])]
+    last = []
+    for r in reversed(mu):
+        last.append(r)
+        if kind_of(r["Kernel_Name"]) == "momentum":
+            break
+    for r in reversed(last):
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        lines.append(f"  {kind_of(r['Kernel_Name']):10s} {dur:9.1f}   {r['Kernel_Name'][:70]}")
+    return "\n".join(lines) + "\n"
+
+
+def _counter_rows(pmc_dir: str, counter: str):
+    rows = list(csv.DictReader(open(_one(os.path.join(pmc_dir, "**", "*counter_collection.csv")))))
+    return [r for r in rows if r["Counter_Name"] == counter]
+
+
+def traffic_summary(fetch_dir: str, write_dir: str, command: str) -> str:
+    out = []
+    scale = {}
+    per_kind = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d, counter)
+        copies = [float(r["Counter_Value"]) for r in rows
+                  if "copy" in r["Kernel_Name"].lower() and int(r["Grid_Size"]) > 0]
+        # the calibration copy is the largest copy kernel of the run
+        kib = max(copies) if copies else None
+        scale[counter] = COPY_BYTES / (kib * 1024.0) if kib else None
+        acc = defaultdict(list)
+        for r in rows:
+            k = kind_of(r["Kernel_Name"])
+            if k:
+                acc[k].append(float(r["Counter_Value"]) * 1024.0)
+        per_kind[counter] = acc
+    out.append("# HBM traffic per dispatch from rocprofv3 counters (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)")
+    out.append(f"# commands: {command}")
+    out.append("# scale = known bytes of a plain 256 MiB copy / bytes the counter reports for it")
+    out.append(f"fetch_scale = {scale['FETCH_SIZE']}")
+    out.append(f"write_scale = {scale['WRITE_SIZE']}")
+    out.append(f"kernel_source_hash = {kernel_source_hash()}")
+    for k in ("momentum", "gram", "poly", "update"):
+        f = per_kind["FETCH_SIZE"].get(k, [])
+        w = per_kind["WRITE_SIZE"].get(k, [])
+        if not f or not w:
+            continue
+        fs = scale["FETCH_SIZE"] or 1.0
+        ws = scale["WRITE_SIZE"] or 1.0
+        fb = sum(f) / len(f) * fs
+        wb = sum(w) / len(w) * ws
+        out.append(f"{k}_fetch_bytes_per_launch = {fb:.0f}")
+        out.append(f"{k}_write_bytes_per_launch = {wb:.0f}")
+        out.append(f"{k}_hbm_bytes_per_launch = {fb + wb:.0f}")
+    return "\n".join(out) + "\n"
+
+
+def main(argv):
+    if argv[0] == "stats":
+        text = stats_summary(argv[1], argv[3])
+        out = argv[2]
+    elif argv[0] == "traffic":
+        text = traffic_summary(argv[1], argv[2], argv[4])
+        out = argv[3]
+    else:
+        raise SystemExit(__doc__)
+    with open(out, "w") as f:
+        f.write(text)
+    print(text)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
