@@ -318,7 +318,7 @@ DevMat make_devmat(const muon_plan* p, int i) {
   r.nparts = g.nparts;
   r.mom_tiles_n = g.mom_n;
   r.scale = d.scale > 0.f ? d.scale : 1.f;
-  r.vec_g = (g.cols % 4 == 0) && ((uintptr_t)d.grad % 16 == 0) && ((uintptr_t)d.momentum % 16 == 0);
+  r.vec_g = (g.cols % 8 == 0) && ((uintptr_t)d.grad % 16 == 0) && ((uintptr_t)d.momentum % 16 == 0);
   r.vec_w = (g.cols % 4 == 0) && ((uintptr_t)d.weight % 16 == 0);
   r.f32 = g.f32;
   return r;

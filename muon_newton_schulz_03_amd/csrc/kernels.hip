@@ -92,9 +92,45 @@ __device__ __forceinline__ float block_inv_norm(const DevMat& d, double* scratch
 
 // ---------------------------------------------------------- momentum ------
 
-// One 64x64 tile of the canonical X per block.  Thread (tx, ty) handles 4
-// consecutive columns of rows ty, ty+16, ty+32, ty+48 of the ORIGINAL tile,
-// so gradient and momentum accesses are coalesced along the original rows.
+// One 64x64 tile of the canonical X per block.  Thread (tx, ty) handles 8
+// consecutive columns of rows ty and ty + 32 of the ORIGINAL tile, so gradient
+// and momentum accesses are 16/32-byte vectors along the original rows; all
+// loads are issued before any store (stores share the in-order counter).
+struct MomRow {
+  float g[8], m[8];
+  bool ok[8];
+  bool vec;
+};
+
+__device__ __forceinline__ void mom_load(const DevMat& d, int r, int c, MomRow& x) {
+  const bool rowok = r < d.rows;
+  const size_t off = (size_t)r * d.cols + c;
+  x.vec = rowok && d.vec_g && c + 7 < d.cols;
+  if (x.vec) {
+    if (d.g_bf16) {
+      const u32x4 gv = *(const u32x4*)((const uint16_t*)d.g + off);
+      unpack4_bf16(u32x2{gv.x, gv.y}, x.g);
+      unpack4_bf16(u32x2{gv.z, gv.w}, x.g + 4);
+    } else {
+      const f32x4 g0 = *(const f32x4*)((const float*)d.g + off), g1 = *(const f32x4*)((const float*)d.g + off + 4);
+      x.g[0] = g0.x; x.g[1] = g0.y; x.g[2] = g0.z; x.g[3] = g0.w;
+      x.g[4] = g1.x; x.g[5] = g1.y; x.g[6] = g1.z; x.g[7] = g1.w;
+    }
+    const f32x4 m0 = *(const f32x4*)(d.mom + off), m1 = *(const f32x4*)(d.mom + off + 4);
+    x.m[0] = m0.x; x.m[1] = m0.y; x.m[2] = m0.z; x.m[3] = m0.w;
+    x.m[4] = m1.x; x.m[5] = m1.y; x.m[6] = m1.z; x.m[7] = m1.w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x.ok[e] = true;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x.ok[e] = rowok && (c + e) < d.cols;
+      x.g[e] = x.ok[e] ? (d.g_bf16 ? bf2f(((const uint16_t*)d.g)[off + e]) : ((const float*)d.g)[off + e]) : 0.f;
+      x.m[e] = x.ok[e] ? d.mom[off + e] : 0.f;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void momentum_kernel(MomArgs args) {
   const Tile tl = args.tiles[blockIdx.x];
   if (tl.mat == kNullMat) return;
@@ -103,86 +139,75 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(MomArgs args) {
   __shared__ float red[kThreads / 64];
 
   const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
+  const int tx = tid & 7, ty = tid >> 3;  // 8 column groups of 8, 32 rows
   const int i0 = tl.ti * kMomTile, j0 = tl.tj * kMomTile;  // canonical origin
   const bool tr = d.transposed != 0;
   const int r0 = tr ? j0 : i0, c0 = tr ? i0 : j0;          // original origin
   const float mu = args.mu;
 
-  float u[4][4];
+  MomRow x[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) mom_load(d, r0 + ty + 32 * q, c0 + 8 * tx, x[q]);
+
+  float u[2][8], mn[2][8];
   float ss = 0.f;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = r0 + ty + 16 * q;
-    const int c = c0 + 4 * tx;
-    float g[4] = {0.f, 0.f, 0.f, 0.f}, m[4] = {0.f, 0.f, 0.f, 0.f};
-    bool ok[4];
-    const bool rowok = r < d.rows;
-    const size_t off = (size_t)r * d.cols + c;
-    if (rowok && d.vec_g && c + 3 < d.cols) {
-      if (d.g_bf16) {
-        unpack4_bf16(*(const u32x2*)((const uint16_t*)d.g + off), g);
-      } else {
-        f32x4 gv = *(const f32x4*)((const float*)d.g + off);
-        g[0] = gv.x; g[1] = gv.y; g[2] = gv.z; g[3] = gv.w;
-      }
-      f32x4 mv = *(const f32x4*)(d.mom + off);
-      m[0] = mv.x; m[1] = mv.y; m[2] = mv.z; m[3] = mv.w;
+  for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ok[e] = true;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ok[e] = rowok && (c + e) < d.cols;
-        if (ok[e]) {
-          g[e] = d.g_bf16 ? bf2f(((const uint16_t*)d.g)[off + e]) : ((const float*)d.g)[off + e];
-          m[e] = d.mom[off + e];
-        }
-      }
-    }
-    float mn[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      mn[e] = fmaf(mu, m[e], g[e]);  // one rounding: fl32(mu*M + G)
-      const float ue = args.nesterov ? fmaf(mu, mn[e], g[e]) : mn[e];
-      u[q][e] = ok[e] ? ue : 0.f;
+    for (int e = 0; e < 8; ++e) {
+      mn[q][e] = fmaf(mu, x[q].m[e], x[q].g[e]);  // one rounding: fl32(mu*M + G)
+      const float ue = args.nesterov ? fmaf(mu, mn[q][e], x[q].g[e]) : mn[q][e];
+      u[q][e] = x[q].ok[e] ? ue : 0.f;
       ss = fmaf(u[q][e], u[q][e], ss);
     }
-    if (rowok && d.vec_g && c + 3 < d.cols) {
-      *(f32x4*)(d.mom + off) = f32x4{mn[0], mn[1], mn[2], mn[3]};
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (ok[e]) d.mom[off + e] = mn[e];
-    }
-  }
 
   // X0 = U in the canonical orientation (zero in the padding).
-  float xv[4][4];
+  float xv[2][8];
   if (tr) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) stage[ty + 16 * q][4 * tx + e] = u[q][e];
+      for (int e = 0; e < 8; ++e) stage[ty + 32 * q][8 * tx + e] = u[q][e];
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) xv[q][e] = stage[4 * tx + e][ty + 16 * q];
+      for (int e = 0; e < 8; ++e) xv[q][e] = stage[8 * tx + e][ty + 32 * q];
   } else {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) xv[q][e] = u[q][e];
+      for (int e = 0; e < 8; ++e) xv[q][e] = u[q][e];
+  }
+
+  // stores: momentum, then X0
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = r0 + ty + 32 * q, c = c0 + 8 * tx;
+    const size_t off = (size_t)r * d.cols + c;
+    if (x[q].vec) {
+      *(f32x4*)(d.mom + off) = f32x4{mn[q][0], mn[q][1], mn[q][2], mn[q][3]};
+      *(f32x4*)(d.mom + off + 4) = f32x4{mn[q][4], mn[q][5], mn[q][6], mn[q][7]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (x[q].ok[e]) d.mom[off + e] = mn[q][e];
+    }
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const size_t xo = (size_t)(i0 + ty + 16 * q) * d.np + j0 + 4 * tx;
+  for (int q = 0; q < 2; ++q) {
+    const size_t xo = (size_t)(i0 + ty + 32 * q) * d.np + j0 + 8 * tx;
     if (d.f32) {
       *(f32x4*)((float*)d.xo[0] + xo) = f32x4{xv[q][0], xv[q][1], xv[q][2], xv[q][3]};
+      *(f32x4*)((float*)d.xo[0] + xo + 4) = f32x4{xv[q][4], xv[q][5], xv[q][6], xv[q][7]};
     } else {
-      *(u32x2*)((uint16_t*)d.xo[0] + xo) = pack4_bf16(xv[q][0], xv[q][1], xv[q][2], xv[q][3]);
-      if (d.x32) *(f32x4*)(d.x32 + xo) = f32x4{xv[q][0], xv[q][1], xv[q][2], xv[q][3]};
+      const u32x2 lo = pack4_bf16(xv[q][0], xv[q][1], xv[q][2], xv[q][3]);
+      const u32x2 hi = pack4_bf16(xv[q][4], xv[q][5], xv[q][6], xv[q][7]);
+      *(u32x4*)((uint16_t*)d.xo[0] + xo) = u32x4{lo.x, lo.y, hi.x, hi.y};
+      if (d.x32) {
+        *(f32x4*)(d.x32 + xo) = f32x4{xv[q][0], xv[q][1], xv[q][2], xv[q][3]};
+        *(f32x4*)(d.x32 + xo + 4) = f32x4{xv[q][4], xv[q][5], xv[q][6], xv[q][7]};
+      }
     }
   }
 

@@ -45,7 +45,7 @@ struct DevMat {
   int32_t nparts;     // number of momentum tiles (= partial sums)
   int32_t mom_tiles_n;// momentum tiles along the canonical n axis
   float scale;        // s of the weight step (already defaulted to 1)
-  int32_t vec_g;      // gradient rows can be read 4 elements at a time
+  int32_t vec_g;      // gradient and momentum rows can be read 8 elements at a time
   int32_t vec_w;      // weight rows can be read/written 4 elements at a time
   int32_t f32;        // this matrix's products use fp32 operands (xo, a, b are fp32)
   int32_t pad_;
