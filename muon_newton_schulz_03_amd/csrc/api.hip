@@ -191,8 +191,10 @@ Tables build_tables(const std::vector<Geometry>& geo) {
       const int tm = g.mp / kTile, tn = g.np / kTile;
       for (int a = 0; a < tm; ++a)
         for (int b = a; b < tm; ++b) sym[i].push_back(Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0});
-      for (int a = 0; a < tm; ++a)
-        for (int b = 0; b < tn; ++b) upd[i].push_back(Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0});
+      // update tiles column by column: the tm tiles of one X column panel run
+      // together and share it in L2
+      for (int b = 0; b < tn; ++b)
+        for (int a = 0; a < tm; ++a) upd[i].push_back(Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0});
       gram_cost[i] = (double)g.np;  // K of each product tile
       poly_cost[i] = (double)g.mp;
       upd_cost[i] = (double)g.mp;

@@ -38,6 +38,20 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Global-memory views of plain pointers.  The pointers in the matrix table are
+// generic; accesses through these views compile to global_* instructions,
+// which count only against the vector-memory counter (flat_* ones would also
+// count against the LDS counter, so every LDS wait would wait for them).
+#define MUON_GLOBAL __attribute__((address_space(1)))
+template <class V, class T>
+__device__ __forceinline__ MUON_GLOBAL V* gv(T* p) {
+  return (MUON_GLOBAL V*)(void*)p;
+}
+template <class V, class T>
+__device__ __forceinline__ const MUON_GLOBAL V* gv(const T* p) {
+  return (const MUON_GLOBAL V*)(const void*)p;
+}
+
 // ---------------------------------------------------------------- helpers --
 
 __device__ __forceinline__ uint16_t f2bf(float x) {
@@ -76,7 +90,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ float block_inv_norm(const DevMat& d, double* scratch, double* nu_out) {
   const int tid = threadIdx.x;
   double s = 0.0;
-  for (int p = tid; p < d.nparts; p += kThreads) s += (double)d.part[p];
+  for (int p = tid; p < d.nparts; p += kThreads) s += (double)gv<float>(d.part)[p];
   scratch[tid] = s;
   __syncthreads();
 #pragma unroll
@@ -108,15 +122,15 @@ __device__ __forceinline__ void mom_load(const DevMat& d, int r, int c, MomRow& 
   x.vec = rowok && d.vec_g && c + 7 < d.cols;
   if (x.vec) {
     if (d.g_bf16) {
-      const u32x4 gv = *(const u32x4*)((const uint16_t*)d.g + off);
-      unpack4_bf16(u32x2{gv.x, gv.y}, x.g);
-      unpack4_bf16(u32x2{gv.z, gv.w}, x.g + 4);
+      const u32x4 g8 = *gv<u32x4>((const uint16_t*)d.g + off);
+      unpack4_bf16(u32x2{g8.x, g8.y}, x.g);
+      unpack4_bf16(u32x2{g8.z, g8.w}, x.g + 4);
     } else {
-      const f32x4 g0 = *(const f32x4*)((const float*)d.g + off), g1 = *(const f32x4*)((const float*)d.g + off + 4);
+      const f32x4 g0 = *gv<f32x4>((const float*)d.g + off), g1 = *gv<f32x4>((const float*)d.g + off + 4);
       x.g[0] = g0.x; x.g[1] = g0.y; x.g[2] = g0.z; x.g[3] = g0.w;
       x.g[4] = g1.x; x.g[5] = g1.y; x.g[6] = g1.z; x.g[7] = g1.w;
     }
-    const f32x4 m0 = *(const f32x4*)(d.mom + off), m1 = *(const f32x4*)(d.mom + off + 4);
+    const f32x4 m0 = *gv<f32x4>(d.mom + off), m1 = *gv<f32x4>(d.mom + off + 4);
     x.m[0] = m0.x; x.m[1] = m0.y; x.m[2] = m0.z; x.m[3] = m0.w;
     x.m[4] = m1.x; x.m[5] = m1.y; x.m[6] = m1.z; x.m[7] = m1.w;
 #pragma unroll
@@ -125,8 +139,9 @@ __device__ __forceinline__ void mom_load(const DevMat& d, int r, int c, MomRow& 
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       x.ok[e] = rowok && (c + e) < d.cols;
-      x.g[e] = x.ok[e] ? (d.g_bf16 ? bf2f(((const uint16_t*)d.g)[off + e]) : ((const float*)d.g)[off + e]) : 0.f;
-      x.m[e] = x.ok[e] ? d.mom[off + e] : 0.f;
+      x.g[e] = x.ok[e] ? (d.g_bf16 ? bf2f(gv<uint16_t>((const uint16_t*)d.g)[off + e]) : gv<float>((const float*)d.g)[off + e])
+                      : 0.f;
+      x.m[e] = x.ok[e] ? gv<float>(d.mom)[off + e] : 0.f;
     }
   }
 }
@@ -134,7 +149,7 @@ __device__ __forceinline__ void mom_load(const DevMat& d, int r, int c, MomRow& 
 __global__ __launch_bounds__(kThreads) void momentum_kernel(MomArgs args) {
   const Tile tl = args.tiles[blockIdx.x];
   if (tl.mat == kNullMat) return;
-  const DevMat& d = args.mats[tl.mat];
+  const DevMat d = args.mats[tl.mat];  // by value: never re-read after a store
   __shared__ float stage[kMomTile][kMomTile + 1];
   __shared__ float red[kThreads / 64];
 
@@ -186,27 +201,27 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(MomArgs args) {
     const int r = r0 + ty + 32 * q, c = c0 + 8 * tx;
     const size_t off = (size_t)r * d.cols + c;
     if (x[q].vec) {
-      *(f32x4*)(d.mom + off) = f32x4{mn[q][0], mn[q][1], mn[q][2], mn[q][3]};
-      *(f32x4*)(d.mom + off + 4) = f32x4{mn[q][4], mn[q][5], mn[q][6], mn[q][7]};
+      *gv<f32x4>(d.mom + off) = f32x4{mn[q][0], mn[q][1], mn[q][2], mn[q][3]};
+      *gv<f32x4>(d.mom + off + 4) = f32x4{mn[q][4], mn[q][5], mn[q][6], mn[q][7]};
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (x[q].ok[e]) d.mom[off + e] = mn[q][e];
+        if (x[q].ok[e]) gv<float>(d.mom)[off + e] = mn[q][e];
     }
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const size_t xo = (size_t)(i0 + ty + 32 * q) * d.np + j0 + 8 * tx;
     if (d.f32) {
-      *(f32x4*)((float*)d.xo[0] + xo) = f32x4{xv[q][0], xv[q][1], xv[q][2], xv[q][3]};
-      *(f32x4*)((float*)d.xo[0] + xo + 4) = f32x4{xv[q][4], xv[q][5], xv[q][6], xv[q][7]};
+      *gv<f32x4>((float*)d.xo[0] + xo) = f32x4{xv[q][0], xv[q][1], xv[q][2], xv[q][3]};
+      *gv<f32x4>((float*)d.xo[0] + xo + 4) = f32x4{xv[q][4], xv[q][5], xv[q][6], xv[q][7]};
     } else {
       const u32x2 lo = pack4_bf16(xv[q][0], xv[q][1], xv[q][2], xv[q][3]);
       const u32x2 hi = pack4_bf16(xv[q][4], xv[q][5], xv[q][6], xv[q][7]);
-      *(u32x4*)((uint16_t*)d.xo[0] + xo) = u32x4{lo.x, lo.y, hi.x, hi.y};
+      *gv<u32x4>((uint16_t*)d.xo[0] + xo) = u32x4{lo.x, lo.y, hi.x, hi.y};
       if (d.x32) {
-        *(f32x4*)(d.x32 + xo) = f32x4{xv[q][0], xv[q][1], xv[q][2], xv[q][3]};
-        *(f32x4*)(d.x32 + xo + 4) = f32x4{xv[q][4], xv[q][5], xv[q][6], xv[q][7]};
+        *gv<f32x4>(d.x32 + xo) = f32x4{xv[q][0], xv[q][1], xv[q][2], xv[q][3]};
+        *gv<f32x4>(d.x32 + xo + 4) = f32x4{xv[q][4], xv[q][5], xv[q][6], xv[q][7]};
       }
     }
   }
@@ -214,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(MomArgs args) {
   ss = wave_sum(ss);
   if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
-  if (tid == 0) d.part[tl.ti * d.mom_tiles_n + tl.tj] = (red[0] + red[1]) + (red[2] + red[3]);
+  if (tid == 0) gv<float>(d.part)[tl.ti * d.mom_tiles_n + tl.tj] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
 // ------------------------------------------------------ weight step -------
@@ -223,13 +238,13 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(MomArgs args) {
 // transposed matrix (the _rows variants take original row R, columns C..C+3).
 // Out-of-range elements load 0 and are not stored.
 __device__ __forceinline__ float wget(const DevMat& d, size_t off) {
-  return d.w_bf16 ? bf2f(((const uint16_t*)d.w)[off]) : ((const float*)d.w)[off];
+  return d.w_bf16 ? bf2f(gv<uint16_t>((const uint16_t*)d.w)[off]) : gv<float>((const float*)d.w)[off];
 }
 __device__ __forceinline__ void wput(const DevMat& d, size_t off, float v) {
   if (d.w_bf16)
-    ((uint16_t*)d.w)[off] = f2bf(v);
+    gv<uint16_t>((uint16_t*)d.w)[off] = f2bf(v);
   else
-    ((float*)d.w)[off] = v;
+    gv<float>((float*)d.w)[off] = v;
 }
 
 // original row R, columns C..C+3
@@ -239,9 +254,9 @@ __device__ __forceinline__ void weight_load_rows(const DevMat& d, int R, int C, 
   const size_t off = (size_t)R * d.cols + C;
   if (d.vec_w && C + 3 < d.cols) {
     if (d.w_bf16) {
-      unpack4_bf16(*(const u32x2*)((const uint16_t*)d.w + off), w);
+      unpack4_bf16(*gv<u32x2>((const uint16_t*)d.w + off), w);
     } else {
-      f32x4 x = *(const f32x4*)((const float*)d.w + off);
+      f32x4 x = __builtin_nontemporal_load(gv<f32x4>((const float*)d.w + off));
       w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
     }
     return;
@@ -255,9 +270,9 @@ __device__ __forceinline__ void weight_store_rows(const DevMat& d, int R, int C,
   const size_t off = (size_t)R * d.cols + C;
   if (d.vec_w && C + 3 < d.cols) {
     if (d.w_bf16)
-      *(u32x2*)((uint16_t*)d.w + off) = pack4_bf16(w[0], w[1], w[2], w[3]);
+      *gv<u32x2>((uint16_t*)d.w + off) = pack4_bf16(w[0], w[1], w[2], w[3]);
     else
-      *(f32x4*)((float*)d.w + off) = f32x4{w[0], w[1], w[2], w[3]};
+      __builtin_nontemporal_store(f32x4{w[0], w[1], w[2], w[3]}, gv<f32x4>((float*)d.w + off));
     return;
   }
 #pragma unroll
@@ -301,7 +316,7 @@ __device__ __forceinline__ void weight_step(const DevMat& d, int i, int j, const
 __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs args) {
   const Tile tl = args.tiles[blockIdx.x];
   if (tl.mat == kNullMat) return;
-  const DevMat& d = args.mats[tl.mat];
+  const DevMat d = args.mats[tl.mat];
   __shared__ double scratch[kThreads];
   const float inv = block_inv_norm(d, scratch, nullptr);
   const float lr_eff = args.lr * d.scale * inv;
@@ -314,19 +329,23 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs args) {
     const size_t xo = (size_t)i * d.np + j;
     float u[4];
     if (d.f32) {
-      f32x4 v = *(const f32x4*)((const float*)d.xo[0] + xo);
+      f32x4 v = *gv<f32x4>((const float*)d.xo[0] + xo);
       u[0] = v.x; u[1] = v.y; u[2] = v.z; u[3] = v.w;
     } else if (d.x32) {
-      f32x4 v = *(const f32x4*)(d.x32 + xo);
+      f32x4 v = *gv<f32x4>(d.x32 + xo);
       u[0] = v.x; u[1] = v.y; u[2] = v.z; u[3] = v.w;
     } else {
-      unpack4_bf16(*(const u32x2*)((const uint16_t*)d.xo[0] + xo), u);
+      unpack4_bf16(*gv<u32x2>((const uint16_t*)d.xo[0] + xo), u);
     }
     weight_step(d, i, j, u, lr_eff);
   }
 }
 
 // ------------------------------------------------ Newton-Schulz stages ----
+
+// Operand copy of X_t (ping-pong by parity).  A select, not an index, keeps
+// the by-value descriptor in registers.
+__device__ __forceinline__ void* xbuf(const DevMat& d, int t) { return (t & 1) ? d.xo[1] : d.xo[0]; }
 
 // Operand slabs go from HBM straight into LDS (gfx950 buffer_load_dwordx4
 // ... lds): each wave instruction moves 64 x 16 bytes into 1 KiB of
@@ -521,17 +540,25 @@ __device__ __forceinline__ void cblock(const float* ct, int c, int r, float (&bl
 template <bool F32>
 __device__ __forceinline__ void store4(void* base, size_t off, const float* v) {
   if (F32)
-    *(f32x4*)((float*)base + off) = f32x4{v[0], v[1], v[2], v[3]};
+    *gv<f32x4>((float*)base + off) = f32x4{v[0], v[1], v[2], v[3]};
   else
-    *(u32x2*)((uint16_t*)base + off) = pack4_bf16(v[0], v[1], v[2], v[3]);
+    *gv<u32x2>((uint16_t*)base + off) = pack4_bf16(v[0], v[1], v[2], v[3]);
+}
+// Streaming form for data that the next kernel, not this one, reads again.
+template <bool F32>
+__device__ __forceinline__ void store4_stream(void* base, size_t off, const float* v) {
+  if (F32)
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, gv<f32x4>((float*)base + off));
+  else
+    __builtin_nontemporal_store(pack4_bf16(v[0], v[1], v[2], v[3]), gv<u32x2>((uint16_t*)base + off));
 }
 template <bool F32>
 __device__ __forceinline__ void load4(const void* base, size_t off, float* v) {
   if (F32) {
-    f32x4 x = *(const f32x4*)((const float*)base + off);
+    f32x4 x = *gv<f32x4>((const float*)base + off);
     v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
   } else {
-    unpack4_bf16(*(const u32x2*)((const uint16_t*)base + off), v);
+    unpack4_bf16(*gv<u32x2>((const uint16_t*)base + off), v);
   }
 }
 
@@ -549,13 +576,13 @@ constexpr int kBlocksPerCu = 2;
 // One block per matrix: s = 1 / (||U||_F + eps) from the momentum kernel's
 // per-tile partial sums (fixed summation order: deterministic).
 __global__ __launch_bounds__(kThreads) void norm_kernel(const DevMat* mats) {
-  const DevMat& d = mats[blockIdx.x];
+  const DevMat d = mats[blockIdx.x];
   __shared__ double scratch[kThreads];
   double nu;
   const float inv = block_inv_norm(d, scratch, &nu);
   if (threadIdx.x == 0) {
-    d.sc[0] = inv;
-    d.sc[1] = (float)nu;
+    gv<float>(d.sc)[0] = inv;
+    gv<float>(d.sc)[1] = (float)nu;
   }
 }
 
@@ -575,9 +602,8 @@ struct TileOps {
 };
 
 template <int STAGE, bool F32>
-__device__ __forceinline__ TileOps tile_ops(const StageArgs& args, const Tile& tl) {
+__device__ __forceinline__ TileOps tile_ops(const StageArgs& args, const DevMat& d, const Tile& tl) {
   constexpr int ES = F32 ? 4 : 2;
-  const DevMat& d = args.mats[tl.mat];
   TileOps o;
   o.mat = tl.mat;
   o.i0 = tl.ti * kTile;
@@ -585,7 +611,7 @@ __device__ __forceinline__ TileOps tile_ops(const StageArgs& args, const Tile& t
   o.qt = tl.ti;
   o.pt = tl.tj;
   o.diag = tl.ti == tl.tj;
-  const char* xin = (const char*)d.xo[(args.t - 1) & 1];
+  const char* xin = (const char*)xbuf(d, args.t - 1);
   int K;
   if (STAGE == 1) {  // A = X X^T: both panels are row panels of X, K = np
     o.qld = o.pld = (uint32_t)d.np * ES;
@@ -634,9 +660,9 @@ __device__ __forceinline__ void store4_upper(void* out, size_t off, const float*
     for (int e = 0; e < 4; ++e)
       if (r <= c + e) {
         if (F32)
-          ((float*)out)[off + e] = v[e];
+          gv<float>((float*)out)[off + e] = v[e];
         else
-          ((uint16_t*)out)[off + e] = f2bf(v[e]);
+          gv<uint16_t>((uint16_t*)out)[off + e] = f2bf(v[e]);
       }
   }
 }
@@ -650,9 +676,9 @@ __device__ __forceinline__ void store4_lower(void* out, size_t off, const float*
     for (int e = 0; e < 4; ++e)
       if (R > cc + e) {
         if (F32)
-          ((float*)out)[off + e] = v[e];
+          gv<float>((float*)out)[off + e] = v[e];
         else
-          ((uint16_t*)out)[off + e] = f2bf(v[e]);
+          gv<uint16_t>((uint16_t*)out)[off + e] = f2bf(v[e]);
       }
   }
 }
@@ -681,16 +707,16 @@ __device__ __forceinline__ void epi_prefetch(const StageArgs& args, const DevMat
   if (STAGE == 2) {
 #pragma unroll
     for (int q = 0; q < 16; ++q)
-      in.dir16[q] = *(const u32x2*)((const uint16_t*)d.a + (size_t)(o.i0 + rbase + 8 * q) * d.mp + o.j0 + c);
+      in.dir16[q] = *gv<u32x2>((const uint16_t*)d.a + (size_t)(o.i0 + rbase + 8 * q) * d.mp + o.j0 + c);
   } else if (STAGE == 3) {
-    const void* xin = d.xo[(args.t - 1) & 1];
+    const void* xin = xbuf(d, args.t - 1);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const size_t off = (size_t)(o.i0 + rbase + 8 * q) * d.np + o.j0 + c;
       if (MODE & kMaster32)
-        in.dir32[q] = *(const f32x4*)(d.x32 + off);
+        in.dir32[q] = __builtin_nontemporal_load(gv<f32x4>(d.x32 + off));
       else
-        in.dir16[q] = *(const u32x2*)((const uint16_t*)xin + off);
+        in.dir16[q] = *gv<u32x2>((const uint16_t*)xin + off);
     }
   }
 }
@@ -704,18 +730,18 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
   const int i0 = o.i0, j0 = o.j0;
 
   float pre = 1.f;  // stage 1 of the first iteration works on U: A = s^2 U U^T
-  if (STAGE == 1 && t == 1) pre = d.sc[0] * d.sc[0];
+  if (STAGE == 1 && t == 1) pre = gv<float>(d.sc)[0] * gv<float>(d.sc)[0];
   float alpha = args.a, beta = 1.f;
   if (STAGE == 3 && t == 1) {
-    alpha = args.a * d.sc[0];
-    beta = d.sc[0];
+    beta = gv<float>(d.sc)[0];
+    alpha = args.a * beta;
   }
   constexpr bool last = STAGE == 3 && (MODE & kLast);
   constexpr bool master32 = STAGE == 3 && !F32 && (MODE & kMaster32);
   const bool write32 = STAGE == 3 && !F32 && !last && t < args.kmaster;
   const float lr_eff = args.lr * d.scale;
-  const void* xin = d.xo[(t - 1) & 1];
-  void* xout = d.xo[t & 1];
+  const void* xin = xbuf(d, t - 1);
+  void* xout = xbuf(d, t);
   void* sym_out = STAGE == 1 ? d.a : d.b;
 
   // ---- stage the tile in LDS (all of it: both K slabs are free now)
@@ -810,8 +836,8 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = fmaf(alpha, xv[e], beta * v[e]);
       if (!last) {
-        store4<F32>(xout, off, v);
-        if (write32) *(f32x4*)(d.x32 + off) = f32x4{v[0], v[1], v[2], v[3]};
+        store4_stream<F32>(xout, off, v);
+        if (write32) __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, gv<f32x4>(d.x32 + off));
       } else if (!d.transposed) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = fmaf(-lr_eff, v[e], wrow[q][e]);
@@ -855,8 +881,8 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void ns_stage_kernel(StageA
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const Tile tl = args.tiles[blockIdx.x];
   if (tl.mat == kNullMat) return;
-  const DevMat& d = args.mats[tl.mat];
-  const TileOps o = tile_ops<STAGE, F32>(args, tl);
+  const DevMat d = args.mats[tl.mat];  // by value: never re-read after a store
+  const TileOps o = tile_ops<STAGE, F32>(args, d, tl);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int w = __builtin_amdgcn_readfirstlane(wave);
