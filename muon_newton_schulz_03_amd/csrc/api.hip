@@ -624,7 +624,10 @@ int muon_step(muon_plan* p, const muon_matrix_desc* descs, int n, float a, float
         const int ntab = (int)p->tab.ns[prec][k].size();
         if (!ntab) continue;
         StageArgs sa{mats, (const Tile*)(p->ws + p->lay.ns_tiles[prec][k]), ntab, t, T, p->opt.kmaster, a, b, c, lr};
-        const int grid = ntab;
+        // persistent grid: two blocks per CU, a multiple of 8 (every block
+        // keeps the XCD of the table entries it takes), never more than the table
+        const int slots = std::max(8, (2 * p->cus) / 8 * 8);
+        const int grid = std::min((ntab + 7) / 8 * 8, slots);
         if ((rc = prof_begin(p, kKinds[k], stream, &pi))) return rc;
         if ((rc = check_launch(launch_stage(k + 1, prec == 1, sa, grid, stream), kNames[k]))) return rc;
         if ((rc = prof_end(p, stream, pi))) return rc;

@@ -598,7 +598,7 @@ struct TileOps {
   int nk;
   int i0, j0;
   int mat;
-  bool diag;
+  int diag;       // a diagonal tile (i0 == j0)
 };
 
 template <int STAGE, bool F32>
@@ -721,10 +721,30 @@ __device__ __forceinline__ void epi_prefetch(const StageArgs& args, const DevMat
   }
 }
 
-template <int STAGE, bool F32, int MODE>
+// The epilogue stages the whole tile in LDS (both ring slots) and then
+// writes it out row by row.  `next_slab` requests the block's next tile's
+// first K slab into ring slot 0: as soon as rows 0..63 (slot 0) have been
+// read back when that is the last use of them (the "early" paths), else at
+// the end.  The number of vector-memory instructions a wave issues after that
+// request (`epilogue_pending`) lets the next tile's first wait leave them in
+// flight: vector-memory operations complete in issue order.
+template <int STAGE, int MODE>
+__device__ __forceinline__ bool epilogue_early(const DevMat& d, const TileOps& o) {
+  if (STAGE == 3) return !((MODE & kLast) && d.transposed);
+  return !o.diag;
+}
+// Lower bound of those instructions: the 8 row-pass stores of rows 64..127
+// on the early paths whose store count does not depend on the data.
+template <int STAGE, int MODE>
+__device__ __forceinline__ int epilogue_pending(const DevMat& d, const TileOps& o) {
+  if (STAGE == 3 && (MODE & kLast)) return 0;
+  return epilogue_early<STAGE, MODE>(d, o) ? 8 : 0;
+}
+
+template <int STAGE, bool F32, int MODE, class NextSlab>
 __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMat& d, const TileOps& o,
                                               const f32x16 (&acc)[2][2], const EpiIn& in, float* ct, int tid, int lane,
-                                              int wm, int wn) {
+                                              int wm, int wn, NextSlab next_slab) {
   const int t = args.t;
   const int c = 4 * (tid & 31), rbase = tid >> 5;
   const int i0 = o.i0, j0 = o.j0;
@@ -743,6 +763,13 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
   const void* xin = xbuf(d, t - 1);
   void* xout = xbuf(d, t);
   void* sym_out = STAGE == 1 ? d.a : d.b;
+  const bool early = epilogue_early<STAGE, MODE>(d, o);
+  auto hand_over = [&](int q) {  // rows 0..63 are no longer read after row pass 7
+    if (q == 8 && early) {
+      MUON_LDS_BARRIER();
+      next_slab();
+    }
+  };
 
   // ---- stage the tile in LDS (all of it: both K slabs are free now)
   {
@@ -778,6 +805,7 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
     // direct tile (i, j)
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
+      hand_over(q);
       const int r = rbase + 8 * q;
       float v[4];
       crow(ct, r, c, v);
@@ -828,6 +856,7 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
     }
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
+      hand_over(q);
       const int r = rbase + 8 * q;
       const size_t off = (size_t)(i0 + r) * d.np + j0 + c;
       float v[4], xv[4];
@@ -869,82 +898,194 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
       MUON_LDS_BARRIER();  // keep the barrier count uniform across the block
     }
   }
+  if (!early) {
+    MUON_LDS_BARRIER();
+    next_slab();
+  }
 }
 
-// One output tile per block.  K slabs stream into a two-slab LDS ring with
-// direct-to-LDS loads: slab kt + 1 is requested right after the barrier that
-// opens slab kt.  The tile's epilogue inputs are requested with the last slab.
+
+// A plain-typed copy of a read-only table entry through the constant address
+// space: uniform addresses then compile to scalar loads, which do not share
+// the in-order vector-memory counter with the epilogue's stores.
+#define MUON_CONST __attribute__((address_space(4)))
+template <class T>
+__device__ __forceinline__ T load_uniform(const T* p) {
+  static_assert(sizeof(T) % 4 == 0, "whole dwords");
+  struct Words {
+    uint32_t w[sizeof(T) / 4];
+  } v;
+  const MUON_CONST uint32_t* s = (const MUON_CONST uint32_t*)(const void*)p;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) v.w[i] = s[i];
+  return __builtin_bit_cast(T, v);
+}
+
+// The descriptor fields the product kernels use (the others stay zero):
+// scalar loads of only these keep the persistent loop within the SGPR budget.
+template <int STAGE, int MODE>
+__device__ __forceinline__ DevMat load_stage_mat(const DevMat* src) {
+  DevMat d = {};
+  d.xo[0] = load_uniform(&src->xo[0]);
+  d.xo[1] = load_uniform(&src->xo[1]);
+  d.a = load_uniform(&src->a);
+  d.mp = load_uniform(&src->mp);
+  d.np = load_uniform(&src->np);
+  if (STAGE != 2) d.sc = load_uniform(&src->sc);
+  if (STAGE >= 2) d.b = load_uniform(&src->b);
+  if (STAGE == 3) {
+    d.x32 = load_uniform(&src->x32);
+    if (MODE & kLast) {
+      d.w = load_uniform(&src->w);
+      d.rows = load_uniform(&src->rows);
+      d.cols = load_uniform(&src->cols);
+      d.m = load_uniform(&src->m);
+      d.n = load_uniform(&src->n);
+      d.transposed = load_uniform(&src->transposed);
+      d.w_bf16 = load_uniform(&src->w_bf16);
+      d.vec_w = load_uniform(&src->vec_w);
+      d.scale = load_uniform(&src->scale);
+    }
+  }
+  return d;
+}
+
+// First table entry at or after q (stepping by `stride`) that is not a null
+// tile; the entry comes back as its 64-bit word (mat | ti << 16 | tj << 32).
+__device__ __forceinline__ int next_entry(const StageArgs& args, int q, int stride, uint64_t& raw) {
+  for (; q < args.ntiles; q += stride) {
+    raw = *(const MUON_CONST uint64_t*)(const void*)(args.tiles + q);
+    if ((raw & 0xFFFFu) != kNullMat) break;
+  }
+  return q;
+}
+__device__ __forceinline__ Tile tile_of(uint64_t raw) {
+  Tile t;
+  t.mat = (uint16_t)raw;
+  t.ti = (uint16_t)(raw >> 16);
+  t.tj = (uint16_t)(raw >> 32);
+  t.pad = 0;
+  return t;
+}
+
+// Persistent product kernel: block b takes the table entries b, b + G,
+// b + 2 G, ... (G = gridDim.x, a multiple of 8, so every entry stays on the
+// XCD the table placed it on).  K slabs stream into a two-slab LDS ring with
+// direct-to-LDS loads, slab kt + 1 requested right after the barrier that
+// opens slab kt; the epilogue's inputs are requested with the last slab, and
+// the next tile's first slab from inside the epilogue (see tile_epilogue).
 template <int STAGE, bool F32, int MODE>
 __global__ __launch_bounds__(kThreads, kBlocksPerCu) void ns_stage_kernel(StageArgs args) {
   constexpr int ES = F32 ? 4 : 2;
   constexpr int BK = 128 / ES;
+  constexpr int kSlabsPerTile = kTile / BK;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const Tile tl = args.tiles[blockIdx.x];
-  if (tl.mat == kNullMat) return;
-  const DevMat d = args.mats[tl.mat];  // by value: never re-read after a store
-  const TileOps o = tile_ops<STAGE, F32>(args, d, tl);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int w = __builtin_amdgcn_readfirstlane(wave);
+  const int stride = gridDim.x;
+  int tid = threadIdx.x, lane = tid & 63;
+
+  uint64_t raw = 0;
+  int q = next_entry(args, blockIdx.x, stride, raw);
+  if (q >= args.ntiles) return;
+  Tile tl = tile_of(raw);
 
   // K slabs below the diagonal of a symmetric operand come first in K order
   // (k < panel * 128), so the loop runs in phases of fixed slab layouts: Q in
   // the X layout for k < qt * 128, P for k < pt * 128 (stage 2, qt <= pt) or
   // always (stage 3, X itself).
   constexpr bool kSymQ = STAGE >= 2, kSymP = STAGE == 2;
-  auto issue = [&](int kt) {
+  auto issue = [&](const TileOps& op, int kt) {
     char* lq = smem + (kt & 1) * kSlabLds;
-    dma_operand<F32>(lq, o.q, o.qld, o.qt, kSymQ, false, kt, w, lane);
-    dma_operand<F32>(lq + kTile * 128, o.p, o.pld, o.pt, kSymP, STAGE == 3, kt, w, lane);
-  };
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int nj = 0; nj < 2; ++nj)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mi][nj][v] = 0.f;
-
-  // All slabs but the last run in the phases; the last slab (always in the
-  // upper triangle: K-contiguous Q, and P too unless it is X) also requests
-  // the epilogue's inputs.
-  auto phase = [&](auto qx, auto px, int kb, int ke) {
-    for (int kt = kb; kt < ke; ++kt) {
-      MUON_WAIT_VMCNT(0);  // this wave's part of slab kt has landed ...
-      MUON_LDS_BARRIER();  // ... everyone's, and slab kt - 1 is no longer read
-      issue(kt + 1);
-      const char* lq = smem + (kt & 1) * kSlabLds;
-      mma_slab<F32, decltype(qx)::value, decltype(px)::value>(acc, lq, lq + kTile * 128, wm, wn, lane);
-    }
+    dma_operand<F32>(lq, op.q, op.qld, op.qt, kSymQ, false, kt, w, lane);
+    dma_operand<F32>(lq + kTile * 128, op.p, op.pld, op.pt, kSymP, STAGE == 3, kt, w, lane);
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
-  constexpr int kSlabsPerTile = kTile / BK;
-  const int nlast = o.nk - 1;
-  issue(0);
-  if (STAGE == 1) {
-    phase(F_{}, F_{}, 0, nlast);
-  } else if (STAGE == 2) {
-    const int kq = o.qt * kSlabsPerTile, kp = o.pt * kSlabsPerTile;
-    phase(T_{}, T_{}, 0, kq);
-    phase(F_{}, T_{}, kq, kp);
-    phase(F_{}, F_{}, kp, nlast);
-  } else {
-    const int kq = o.qt * kSlabsPerTile;
-    phase(T_{}, T_{}, 0, kq);
-    phase(F_{}, T_{}, kq, nlast);
+
+  DevMat d = load_stage_mat<STAGE, MODE>(args.mats + tl.mat);
+  TileOps o = tile_ops<STAGE, F32>(args, d, tl);
+  int pend = 0;  // vector-memory operations issued after the request of this tile's slab 0
+  issue(o, 0);
+  for (;;) {
+    // Opaque per tile: lane-derived addresses are recomputed for each tile
+    // instead of being kept live through the epilogue.
+    asm volatile("" : "+v"(tid), "+v"(lane));
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < 2; ++nj)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[mi][nj][v] = 0.f;
+
+    // All slabs but the last run in the phases; the last slab (always in the
+    // upper triangle: K-contiguous Q, and P too unless it is X) also requests
+    // the epilogue's inputs.
+    auto phase = [&](auto qx, auto px, int kb, int ke) {
+      for (int kt = kb; kt < ke; ++kt) {
+        if (kt == 0 && pend >= 8)
+          MUON_WAIT_VMCNT(8);  // slab 0 has landed; the last epilogue's final stores may not have
+        else
+          MUON_WAIT_VMCNT(0);  // this wave's part of slab kt has landed ...
+        MUON_LDS_BARRIER();    // ... everyone's, and slab kt - 1 is no longer read
+        issue(o, kt + 1);
+        const char* lq = smem + (kt & 1) * kSlabLds;
+        mma_slab<F32, decltype(qx)::value, decltype(px)::value>(acc, lq, lq + kTile * 128, wm, wn, lane);
+      }
+    };
+    const int nlast = o.nk - 1;
+    if (STAGE == 1) {
+      phase(F_{}, F_{}, 0, nlast);
+    } else if (STAGE == 2) {
+      const int kq = o.qt * kSlabsPerTile, kp = o.pt * kSlabsPerTile;
+      phase(T_{}, T_{}, 0, kq);
+      phase(F_{}, T_{}, kq, kp);
+      phase(F_{}, F_{}, kp, nlast);
+    } else {
+      const int kq = o.qt * kSlabsPerTile;
+      phase(T_{}, T_{}, 0, kq);
+      phase(F_{}, T_{}, kq, nlast);
+    }
+    // the next tile of this block (scalar loads, overlapping the last slab)
+    uint64_t rawn = 0;
+    const int qn = next_entry(args, q + stride, stride, rawn);
+    const bool more = qn < args.ntiles;
+    const Tile tn = tile_of(rawn);
+    TileOps on = o;
+    if (more) {
+      // only what the first slab's request needs; the rest is read after the epilogue
+      DevMat dn = {};
+      const DevMat* src = args.mats + tn.mat;
+      dn.xo[0] = load_uniform(&src->xo[0]);
+      dn.xo[1] = load_uniform(&src->xo[1]);
+      if (STAGE == 2) dn.a = load_uniform(&src->a);
+      if (STAGE == 3) dn.b = load_uniform(&src->b);
+      dn.mp = load_uniform(&src->mp);
+      dn.np = load_uniform(&src->np);
+      on = tile_ops<STAGE, F32>(args, dn, tn);
+    }
+    EpiIn in;
+    {
+      MUON_WAIT_VMCNT(0);
+      MUON_LDS_BARRIER();
+      epi_prefetch<STAGE, F32, MODE>(args, d, o, in, tid);
+      const char* lq = smem + (nlast & 1) * kSlabLds;
+      mma_slab<F32, false, STAGE == 3>(acc, lq, lq + kTile * 128, wm, wn, lane);
+    }
+    MUON_LDS_BARRIER();  // the last slab has been read by all: LDS holds the staged tile next
+    tile_epilogue<STAGE, F32, MODE>(args, d, o, acc, in, (float*)smem, tid, lane, wm, wn, [&] {
+      if (more) issue(on, 0);
+      asm volatile("" ::: "memory");  // the epilogue's later memory operations stay after the request
+    });
+    if (!more) break;
+    pend = epilogue_pending<STAGE, MODE>(d, o);
+    q = qn;
+    tl = tn;
+    d = load_stage_mat<STAGE, MODE>(args.mats + tl.mat);
+    o = on;
   }
-  EpiIn in;
-  {
-    MUON_WAIT_VMCNT(0);
-    MUON_LDS_BARRIER();
-    epi_prefetch<STAGE, F32, MODE>(args, d, o, in, tid);
-    const char* lq = smem + (nlast & 1) * kSlabLds;
-    mma_slab<F32, false, STAGE == 3>(acc, lq, lq + kTile * 128, wm, wn, lane);
-  }
-  MUON_LDS_BARRIER();  // the last slab has been read by all: LDS holds the staged tile next
-  tile_epilogue<STAGE, F32, MODE>(args, d, o, acc, in, (float*)smem, tid, lane, wm, wn);
 }
 
 hipError_t launch_norm(const DevMat* mats, int n, hipStream_t stream) {
