@@ -45,9 +45,9 @@ def work_model(shapes, T):
 
 
 def momentum_bytes(shapes, master: bool):
-    """Algorithmic HBM bytes of the momentum kernel: G (bf16) + M read/write + X0 (bf16 [+ fp32])."""
+    """Algorithmic HBM bytes of the momentum kernel: G (bf16) + M read/write + X0 (bf16 [+ bf16 low word])."""
     p = sum(r * c for r, c in shapes)
-    return p * (2 + 4 + 4 + 2 + (4 if master else 0))
+    return p * (2 + 4 + 4 + 2 + (2 if master else 0))
 
 
 def read_traffic(kind: str):

@@ -108,7 +108,7 @@ int check_desc(const muon_matrix_desc& d, int idx, bool need_ptrs) {
 struct Layout {
   // per matrix byte offsets into the workspace
   struct M {
-    size_t x32, xo0, xo1, a, b, part, sc;
+    size_t xlo, xo0, xo1, a, b, part, sc;
   };
   std::vector<M> m;
   size_t slots = 0, slot_bytes = 0;
@@ -230,10 +230,10 @@ size_t layout(const std::vector<Geometry>& geo, const Options& o, const Tables& 
     const size_t es = g.f32 ? 4 : 2;
     const size_t xe = (size_t)g.mp * g.np, ae = (size_t)g.mp * g.mp;
     Layout::M& m = L->m[i];
-    m.x32 = (size_t)-1;
+    m.xlo = (size_t)-1;
     if (!g.f32 && o.kmaster > 0) {
-      m.x32 = off;
-      off = align_up(off + xe * 4, kAlign);
+      m.xlo = off;
+      off = align_up(off + xe * 2, kAlign);
     }
     m.xo0 = off;
     off = align_up(off + xe * es, kAlign);
@@ -301,7 +301,7 @@ DevMat make_devmat(const muon_plan* p, int i) {
   r.w = d.weight;
   r.g = d.grad;
   r.mom = d.momentum;
-  r.x32 = m.x32 == (size_t)-1 ? nullptr : (float*)(p->ws + m.x32);
+  r.xlo = m.xlo == (size_t)-1 ? nullptr : (uint16_t*)(p->ws + m.xlo);
   r.xo[0] = p->ws + m.xo0;
   r.xo[1] = p->ws + m.xo1;
   r.a = p->ws + m.a;

@@ -59,6 +59,10 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
   return __builtin_bit_cast(uint16_t, h);
 }
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+// Low word of the hi/lo bf16 pair that carries X in more precision than one
+// bf16: hi = bf16(x) is the operand copy itself, lo = bf16(x - hi) (x - hi is
+// exact in fp32), and hi + lo holds about 16 significant bits of x.
+__device__ __forceinline__ float lo_part(float x) { return x - bf2f(f2bf(x)); }
 
 __device__ __forceinline__ u32x2 pack4_bf16(float a, float b, float c, float d) {
   u32x2 r;
@@ -216,12 +220,13 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(MomArgs args) {
       *gv<f32x4>((float*)d.xo[0] + xo) = f32x4{xv[q][0], xv[q][1], xv[q][2], xv[q][3]};
       *gv<f32x4>((float*)d.xo[0] + xo + 4) = f32x4{xv[q][4], xv[q][5], xv[q][6], xv[q][7]};
     } else {
-      const u32x2 lo = pack4_bf16(xv[q][0], xv[q][1], xv[q][2], xv[q][3]);
-      const u32x2 hi = pack4_bf16(xv[q][4], xv[q][5], xv[q][6], xv[q][7]);
-      *gv<u32x4>((uint16_t*)d.xo[0] + xo) = u32x4{lo.x, lo.y, hi.x, hi.y};
-      if (d.x32) {
-        *gv<f32x4>(d.x32 + xo) = f32x4{xv[q][0], xv[q][1], xv[q][2], xv[q][3]};
-        *gv<f32x4>(d.x32 + xo + 4) = f32x4{xv[q][4], xv[q][5], xv[q][6], xv[q][7]};
+      const u32x2 h0 = pack4_bf16(xv[q][0], xv[q][1], xv[q][2], xv[q][3]);
+      const u32x2 h1 = pack4_bf16(xv[q][4], xv[q][5], xv[q][6], xv[q][7]);
+      *gv<u32x4>((uint16_t*)d.xo[0] + xo) = u32x4{h0.x, h0.y, h1.x, h1.y};
+      if (d.xlo) {
+        const u32x2 l0 = pack4_bf16(lo_part(xv[q][0]), lo_part(xv[q][1]), lo_part(xv[q][2]), lo_part(xv[q][3]));
+        const u32x2 l1 = pack4_bf16(lo_part(xv[q][4]), lo_part(xv[q][5]), lo_part(xv[q][6]), lo_part(xv[q][7]));
+        *gv<u32x4>(d.xlo + xo) = u32x4{l0.x, l0.y, l1.x, l1.y};
       }
     }
   }
@@ -331,11 +336,14 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs args) {
     if (d.f32) {
       f32x4 v = *gv<f32x4>((const float*)d.xo[0] + xo);
       u[0] = v.x; u[1] = v.y; u[2] = v.z; u[3] = v.w;
-    } else if (d.x32) {
-      f32x4 v = *gv<f32x4>(d.x32 + xo);
-      u[0] = v.x; u[1] = v.y; u[2] = v.z; u[3] = v.w;
     } else {
       unpack4_bf16(*gv<u32x2>((const uint16_t*)d.xo[0] + xo), u);
+      if (d.xlo) {
+        float l[4];
+        unpack4_bf16(*gv<u32x2>(d.xlo + xo), l);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] += l[e];
+      }
     }
     weight_step(d, i, j, u, lr_eff);
   }
@@ -684,19 +692,19 @@ __device__ __forceinline__ void store4_lower(void* out, size_t off, const float*
 }
 
 // Inputs of a tile's epilogue, prefetched while its last K slab multiplies
-// (bf16 products): A at the direct and mirror positions (stage 2), the
-// master X (stage 3; fp32 copy or bf16).  Global stores share the in-order
+// (bf16 products): A at the direct positions (stage 2), X (stage 3: its
+// bf16 copy, plus the low words in the kHiLo variant).  Global stores share the in-order
 // vector-memory counter with loads, so every load of the epilogue is issued
 // before its first store.  Row pass: thread handles tile rows (tid >> 5) + 8 q
 // and columns c..c+3; column pass: the 4x4 block C[c..c+3][r..r+3] with
 // r = 4 (tid >> 5) + 32 q, written as 4 rows of the transposed tile.
-// Stage 3 kernels come in variants: kMaster32 (the a*X term reads the fp32
-// copy of X) and kLast (last iteration: the weight step instead of storing X).
-constexpr int kMaster32 = 1, kLast = 2;
+// Stage 3 kernels come in variants: kHiLo (the a*X term reads X as its
+// hi/lo bf16 pair) and kLast (last iteration: the weight step instead of storing X).
+constexpr int kHiLo = 1, kLast = 2;
 
 struct EpiIn {
-  u32x2 dir16[16];  // bf16 at the direct positions (A of stage 2, master X of stage 3)
-  f32x4 dir32[16];  // fp32 master X (stage 3, kMaster32)
+  u32x2 dir16[16];  // bf16 at the direct positions (A of stage 2, X of stage 3)
+  u32x2 lo16[16];   // low words of X (stage 3, kHiLo)
 };
 
 template <int STAGE, bool F32, int MODE>
@@ -713,10 +721,8 @@ __device__ __forceinline__ void epi_prefetch(const StageArgs& args, const DevMat
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const size_t off = (size_t)(o.i0 + rbase + 8 * q) * d.np + o.j0 + c;
-      if (MODE & kMaster32)
-        in.dir32[q] = __builtin_nontemporal_load(gv<f32x4>(d.x32 + off));
-      else
-        in.dir16[q] = *gv<u32x2>((const uint16_t*)xin + off);
+      in.dir16[q] = *gv<u32x2>((const uint16_t*)xin + off);
+      if (MODE & kHiLo) in.lo16[q] = __builtin_nontemporal_load(gv<u32x2>(d.xlo + off));
     }
   }
 }
@@ -757,8 +763,8 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
     alpha = args.a * beta;
   }
   constexpr bool last = STAGE == 3 && (MODE & kLast);
-  constexpr bool master32 = STAGE == 3 && !F32 && (MODE & kMaster32);
-  const bool write32 = STAGE == 3 && !F32 && !last && t < args.kmaster;
+  constexpr bool hilo_in = STAGE == 3 && !F32 && (MODE & kHiLo);
+  const bool write_lo = STAGE == 3 && !F32 && !last && t < args.kmaster;
   const float lr_eff = args.lr * d.scale;
   const void* xin = xbuf(d, t - 1);
   void* xout = xbuf(d, t);
@@ -792,10 +798,14 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
       const size_t off = STAGE == 2 ? (size_t)(i0 + rbase + 8 * q) * d.mp + j0 + c
                                     : (size_t)(i0 + rbase + 8 * q) * d.np + j0 + c;
       load4<true>(STAGE == 2 ? (const void*)d.a : xin, off, v);
-    } else if (master32) {
-      v[0] = in.dir32[q].x; v[1] = in.dir32[q].y; v[2] = in.dir32[q].z; v[3] = in.dir32[q].w;
     } else {
       unpack4_bf16(in.dir16[q], v);
+      if (hilo_in) {
+        float l[4];
+        unpack4_bf16(in.lo16[q], l);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += l[e];
+      }
     }
   };
 
@@ -866,7 +876,9 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
       for (int e = 0; e < 4; ++e) v[e] = fmaf(alpha, xv[e], beta * v[e]);
       if (!last) {
         store4_stream<F32>(xout, off, v);
-        if (write32) __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, gv<f32x4>(d.x32 + off));
+        if (write_lo)
+          __builtin_nontemporal_store(pack4_bf16(lo_part(v[0]), lo_part(v[1]), lo_part(v[2]), lo_part(v[3])),
+                                      gv<u32x2>(d.xlo + off));
       } else if (!d.transposed) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = fmaf(-lr_eff, v[e], wrow[q][e]);
@@ -934,7 +946,7 @@ __device__ __forceinline__ DevMat load_stage_mat(const DevMat* src) {
   if (STAGE != 2) d.sc = load_uniform(&src->sc);
   if (STAGE >= 2) d.b = load_uniform(&src->b);
   if (STAGE == 3) {
-    d.x32 = load_uniform(&src->x32);
+    d.xlo = load_uniform(&src->xlo);
     if (MODE & kLast) {
       d.w = load_uniform(&src->w);
       d.rows = load_uniform(&src->rows);
@@ -1126,7 +1138,7 @@ hipError_t prepare_stage_kernels() {
 
 hipError_t launch_stage(int stage, bool f32, const StageArgs& args, int blocks, hipStream_t stream) {
   const bool last = args.t == args.T;
-  const bool m32 = !f32 && args.t <= args.kmaster;
+  const bool hilo = !f32 && args.t <= args.kmaster;
   if (stage == 1) {
     if (f32) { MUON_STAGE_LAUNCH(1, true, 0) }
     MUON_STAGE_LAUNCH(1, false, 0)
@@ -1141,10 +1153,10 @@ hipError_t launch_stage(int stage, bool f32, const StageArgs& args, int blocks, 
       MUON_STAGE_LAUNCH(3, true, 0)
     }
     if (last) {
-      if (m32) { MUON_STAGE_LAUNCH(3, false, 3) }
+      if (hilo) { MUON_STAGE_LAUNCH(3, false, 3) }
       MUON_STAGE_LAUNCH(3, false, 2)
     }
-    if (m32) { MUON_STAGE_LAUNCH(3, false, 1) }
+    if (hilo) { MUON_STAGE_LAUNCH(3, false, 1) }
     MUON_STAGE_LAUNCH(3, false, 0)
   }
   return hipErrorInvalidValue;

@@ -30,7 +30,7 @@ struct DevMat {
   void* w;            // weights (rows x cols), f32 or bf16
   const void* g;      // gradient (rows x cols), f32 or bf16
   float* mom;         // momentum (rows x cols), f32
-  float* x32;         // bf16 path: fp32 master copy of X (mp x np); else null
+  uint16_t* xlo;      // bf16 path: low word of X, bf16(X - bf16(X)) (mp x np); else null
   void* xo[2];        // operand copies of X (ping-pong), bf16 or f32, mp x np
   void* a;            // A = X X^T, mp x mp (bf16 or f32)
   void* b;            // B = b A + c A A, mp x mp
@@ -64,7 +64,7 @@ struct StageArgs {
   int32_t ntiles;   // table length (persistent blocks stride through it)
   int32_t t;        // iteration, 1-based
   int32_t T;        // iterations this step
-  int32_t kmaster;  // bf16 path: iterations 1..kmaster read the fp32 master in a*X
+  int32_t kmaster;  // bf16 path: iterations 1..kmaster read X as its hi/lo bf16 pair in a*X
   float a, b, c;
   float lr;
 };
