@@ -24,7 +24,7 @@ KIND_COUNT = 6
 KIND_NAMES = ("momentum", "gram", "poly", "update", "apply", "norm")
 
 EXPORTS = ("muon_version", "muon_workspace_size", "muon_init", "muon_step", "muon_destroy",
-           "muon_last_error", "muon_describe", "muon_profile_enable", "muon_profile_read")
+           "muon_last_error", "muon_describe", "muon_profile_enable", "muon_profile_select", "muon_profile_read")
 
 
 class MatrixDesc(ctypes.Structure):
@@ -88,6 +88,8 @@ def load(path: str = None) -> ctypes.CDLL:
                                   P(ctypes.c_int32), ctypes.c_int, P(ctypes.c_int32)]
     lib.muon_profile_enable.restype = ctypes.c_int
     lib.muon_profile_enable.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    lib.muon_profile_select.restype = ctypes.c_int
+    lib.muon_profile_select.argtypes = [ctypes.c_void_p, ctypes.c_uint32]
     lib.muon_profile_read.restype = ctypes.c_int
     lib.muon_profile_read.argtypes = [ctypes.c_void_p, P(ctypes.c_double), P(ctypes.c_int64)]
     _lib = lib

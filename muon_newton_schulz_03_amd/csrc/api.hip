@@ -284,6 +284,7 @@ struct muon_plan {
   // profiling
   bool prof = false;
   std::vector<hipEvent_t> pev;         // pairs: start, stop
+  uint32_t pmask = ~0u;                // kinds whose launches are timed
   std::vector<int> pkind;              // kind of each pair
   size_t pused = 0;
   double pms[MUON_KIND_COUNT] = {};
@@ -353,8 +354,11 @@ int note_slot_use(muon_plan* p, hipStream_t stream) {
   return MUON_OK;
 }
 
+constexpr size_t kNoProfile = ~(size_t)0;
+
 int prof_begin(muon_plan* p, int kind, hipStream_t stream, size_t* idx) {
-  if (!p->prof) return MUON_OK;
+  *idx = kNoProfile;
+  if (!p->prof || !((p->pmask >> kind) & 1u)) return MUON_OK;
   if (p->pused * 2 + 2 > p->pev.size()) {
     for (int k = 0; k < 64; ++k) {
       hipEvent_t ev;
@@ -372,7 +376,7 @@ int prof_begin(muon_plan* p, int kind, hipStream_t stream, size_t* idx) {
 }
 
 int prof_end(muon_plan* p, hipStream_t stream, size_t idx) {
-  if (!p->prof) return MUON_OK;
+  if (!p->prof || idx == kNoProfile) return MUON_OK;
   hipError_t e = hipEventRecord(p->pev[2 * idx + 1], stream);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord(profile)");
   return MUON_OK;
@@ -655,6 +659,13 @@ int muon_profile_enable(muon_plan* p, int enable) {
   g_err.clear();
   if (!p) return fail(MUON_E_INVAL, "plan is NULL");
   p->prof = enable != 0;
+  return MUON_OK;
+}
+
+int muon_profile_select(muon_plan* p, uint32_t kind_mask) {
+  g_err.clear();
+  if (!p) return fail(MUON_E_INVAL, "plan is NULL");
+  p->pmask = kind_mask;
   return MUON_OK;
 }
 

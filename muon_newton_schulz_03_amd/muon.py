@@ -140,7 +140,10 @@ class MuonStep:
         _lib.check(self._lib.muon_step(self._plan, descs, self.n, a, b, c, int(T), momentum, int(bool(nesterov)),
                                        lr, ctypes.c_void_p(stream)))
 
-    def profile(self, enable: bool = True) -> None:
+    def profile(self, enable: bool = True, kinds: Optional[Sequence[str]] = None) -> None:
+        """Time launches with HIP events; ``kinds`` (names from KIND_NAMES) limits which."""
+        mask = 0xFFFFFFFF if kinds is None else sum(1 << _lib.KIND_NAMES.index(k) for k in kinds)
+        _lib.check(self._lib.muon_profile_select(self._plan, mask))
         _lib.check(self._lib.muon_profile_enable(self._plan, int(enable)))
 
     def read_profile(self) -> Dict[str, Tuple[float, int]]:
