@@ -158,10 +158,15 @@ typedef struct muon_plan_info {
   int32_t blocks[MUON_KIND_COUNT]; /* tile-table length of each launch kind: the grid of
                                       the momentum, norm and apply launches; the product
                                       kernels are persistent (2 blocks per CU) and
-                                      stride through their table */
+                                      stride through their table (all groups' tables,
+                                      each padded to a multiple of 8) */
   int32_t x_master_iters;
   int32_t path;
   int32_t n_f32_matrices;    /* matrices whose products run in fp32 (see below) */
+  int32_t n_groups;          /* matrix groups whose Newton-Schulz launches run on
+                                their own streams (1 or 2): a product kind has
+                                T * n_groups launches per step, plus one per
+                                group for each precision beyond the first */
 } muon_plan_info;
 
 int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts,

@@ -42,7 +42,7 @@ class Options(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [("workspace_bytes", ctypes.c_int64), ("n_matrices", ctypes.c_int32), ("tile", ctypes.c_int32),
                 ("blocks", ctypes.c_int32 * KIND_COUNT), ("x_master_iters", ctypes.c_int32),
-                ("path", ctypes.c_int32), ("n_f32_matrices", ctypes.c_int32)]
+                ("path", ctypes.c_int32), ("n_f32_matrices", ctypes.c_int32), ("n_groups", ctypes.c_int32)]
 
 
 class MuonError(RuntimeError):

@@ -105,6 +105,11 @@ int check_desc(const muon_matrix_desc& d, int idx, bool need_ptrs) {
   return MUON_OK;
 }
 
+// The Newton-Schulz launches of the two matrix groups (contiguous halves of
+// equal cost) go to two streams: each group's kernels fill the other's
+// launch gaps and end-of-launch tails.
+constexpr int kGroups = 2;
+
 struct Layout {
   // per matrix byte offsets into the workspace
   struct M {
@@ -113,7 +118,7 @@ struct Layout {
   std::vector<M> m;
   size_t slots = 0, slot_bytes = 0;
   size_t mom_tiles = 0;
-  size_t ns_tiles[2][3] = {};
+  size_t ns_tiles[kGroups][2][3] = {};
   size_t total = 0;
 };
 
@@ -142,7 +147,7 @@ Geometry geometry(const muon_matrix_desc& d, int path) {
 enum { kGram = 0, kPoly = 1, kUpd = 2 };
 struct Tables {
   std::vector<Tile> mom;
-  std::vector<Tile> ns[2][3];
+  std::vector<Tile> ns[kGroups][2][3];  // [group][precision][kind]
 };
 
 // Tiles of one kind, ordered for the MI355X dispatcher, which places block b
@@ -179,15 +184,33 @@ std::vector<Tile> xcd_order(const std::vector<std::vector<Tile>>& per_mat, const
   return out;
 }
 
+// Matrices [0, split) form group 0 and [split, n) group 1, split where the
+// running Newton-Schulz cost is closest to half (a single matrix: group 1 is empty).
+int group_split(const std::vector<Geometry>& geo) {
+  const int nm = (int)geo.size();
+  if (nm < 2) return nm;
+  std::vector<double> pre(nm + 1, 0.0);
+  for (int i = 0; i < nm; ++i) {
+    const double m = geo[i].mp, n = geo[i].np;
+    pre[i + 1] = pre[i] + m * m * (2.0 * n + m);
+  }
+  int best = 1;
+  for (int s = 1; s < nm; ++s)
+    if (std::fabs(2.0 * pre[s] - pre[nm]) < std::fabs(2.0 * pre[best] - pre[nm])) best = s;
+  return best;
+}
+
 Tables build_tables(const std::vector<Geometry>& geo) {
   Tables t;
   const int nm = (int)geo.size();
+  const int split = group_split(geo);
+  for (int grp = 0; grp < kGroups; ++grp)
   for (int prec = 0; prec < 2; ++prec) {
     std::vector<std::vector<Tile>> sym(nm), upd(nm);
     std::vector<double> gram_cost(nm), poly_cost(nm), upd_cost(nm);
     for (int i = 0; i < nm; ++i) {
       const Geometry& g = geo[i];
-      if (g.f32 != prec) continue;
+      if (g.f32 != prec || (i < split) != (grp == 0)) continue;
       const int tm = g.mp / kTile, tn = g.np / kTile;
       for (int a = 0; a < tm; ++a)
         for (int b = a; b < tm; ++b) sym[i].push_back(Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0});
@@ -199,9 +222,9 @@ Tables build_tables(const std::vector<Geometry>& geo) {
       poly_cost[i] = (double)g.mp;
       upd_cost[i] = (double)g.mp;
     }
-    t.ns[prec][kGram] = xcd_order(sym, gram_cost);
-    t.ns[prec][kPoly] = xcd_order(sym, poly_cost);
-    t.ns[prec][kUpd] = xcd_order(upd, upd_cost);
+    t.ns[grp][prec][kGram] = xcd_order(sym, gram_cost);
+    t.ns[grp][prec][kPoly] = xcd_order(sym, poly_cost);
+    t.ns[grp][prec][kUpd] = xcd_order(upd, upd_cost);
   }
   for (int i = 0; i < nm; ++i) {
     const Geometry& g = geo[i];
@@ -219,11 +242,12 @@ size_t layout(const std::vector<Geometry>& geo, const Options& o, const Tables& 
   off += L->slot_bytes * kSlots;
   L->mom_tiles = off;
   off = align_up(off + sizeof(Tile) * t.mom.size(), kAlign);
-  for (int prec = 0; prec < 2; ++prec)
-    for (int k = 0; k < 3; ++k) {
-      L->ns_tiles[prec][k] = off;
-      off = align_up(off + sizeof(Tile) * t.ns[prec][k].size(), kAlign);
-    }
+  for (int grp = 0; grp < kGroups; ++grp)
+    for (int prec = 0; prec < 2; ++prec)
+      for (int k = 0; k < 3; ++k) {
+        L->ns_tiles[grp][prec][k] = off;
+        off = align_up(off + sizeof(Tile) * t.ns[grp][prec][k].size(), kAlign);
+      }
   L->m.resize(nm);
   for (int i = 0; i < nm; ++i) {
     const Geometry& g = geo[i];
@@ -281,6 +305,8 @@ struct muon_plan {
   int slot = 0;
   hipEvent_t last_ev = nullptr;        // recorded after the last enqueued work
   bool last_valid = false;
+  hipStream_t gs[kGroups] = {};        // the groups' Newton-Schulz streams (default priority)
+  hipEvent_t fork_ev = nullptr, join_ev[kGroups] = {};
   // profiling
   bool prof = false;
   std::vector<hipEvent_t> pev;         // pairs: start, stop
@@ -406,6 +432,20 @@ size_t muon_workspace_size(const muon_matrix_desc* descs, int n, const muon_opti
   return layout(geo, o, t, &L);
 }
 
+// All launches of one product kind, table after table, each padded with null
+// tiles to a multiple of 8 so that entry b of the result still runs on XCD b % 8.
+static std::vector<Tile> concat_tables(const Tables& t, int k) {
+  std::vector<Tile> v;
+  for (int grp = 0; grp < kGroups; ++grp)
+    for (int prec = 0; prec < 2; ++prec) {
+      const std::vector<Tile>& s = t.ns[grp][prec][k];
+      if (s.empty()) continue;
+      if (!v.empty()) v.resize((v.size() + kXcds - 1) / kXcds * kXcds, Tile{kNullMat, 0, 0, 0});
+      v.insert(v.end(), s.begin(), s.end());
+    }
+  return v;
+}
+
 int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts, muon_plan_info* info, int kind,
                   int32_t* tiles, int tile_cap, int32_t* n_tiles) {
   g_err.clear();
@@ -424,9 +464,9 @@ int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts
     info->n_matrices = n;
     info->tile = kTile;
     info->blocks[MUON_KIND_MOMENTUM] = (int32_t)t.mom.size();
-    info->blocks[MUON_KIND_GRAM] = (int32_t)(t.ns[0][kGram].size() + t.ns[1][kGram].size());
-    info->blocks[MUON_KIND_POLY] = (int32_t)(t.ns[0][kPoly].size() + t.ns[1][kPoly].size());
-    info->blocks[MUON_KIND_UPDATE] = (int32_t)(t.ns[0][kUpd].size() + t.ns[1][kUpd].size());
+    info->blocks[MUON_KIND_GRAM] = (int32_t)concat_tables(t, kGram).size();
+    info->blocks[MUON_KIND_POLY] = (int32_t)concat_tables(t, kPoly).size();
+    info->blocks[MUON_KIND_UPDATE] = (int32_t)concat_tables(t, kUpd).size();
     info->blocks[MUON_KIND_APPLY] = (int32_t)t.mom.size();
     info->blocks[MUON_KIND_NORM] = n;
     info->x_master_iters = o.kmaster;
@@ -434,6 +474,9 @@ int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts
     int nf = 0;
     for (const Geometry& g : geo) nf += g.f32;
     info->n_f32_matrices = nf;
+    int ng = 0;
+    for (int grp = 0; grp < kGroups; ++grp) ng += !t.ns[grp][0][kUpd].empty() || !t.ns[grp][1][kUpd].empty();
+    info->n_groups = ng;
   }
   if (kind >= 0) {
     std::vector<Tile> v;
@@ -444,8 +487,7 @@ int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts
       case MUON_KIND_POLY:
       case MUON_KIND_UPDATE: {
         const int k = kind == MUON_KIND_GRAM ? kGram : kind == MUON_KIND_POLY ? kPoly : kUpd;
-        v = t.ns[0][k];
-        v.insert(v.end(), t.ns[1][k].begin(), t.ns[1][k].end());
+        v = concat_tables(t, k);
         break;
       }
       default: return fail(MUON_E_INVAL, "kind %d unknown", kind);
@@ -506,6 +548,14 @@ int muon_init(const muon_matrix_desc* descs, int n, const muon_options* opts, vo
   }
   hipError_t e = hipEventCreateWithFlags(&p->last_ev, hipEventDisableTiming);
   if (e != hipSuccess) return cleanup(hip_fail(e, "hipEventCreate"));
+  e = hipEventCreateWithFlags(&p->fork_ev, hipEventDisableTiming);
+  if (e != hipSuccess) return cleanup(hip_fail(e, "hipEventCreate"));
+  for (int g = 0; g < kGroups; ++g) {
+    e = hipStreamCreateWithFlags(&p->gs[g], hipStreamNonBlocking);
+    if (e != hipSuccess) return cleanup(hip_fail(e, "hipStreamCreate"));
+    e = hipEventCreateWithFlags(&p->join_ev[g], hipEventDisableTiming);
+    if (e != hipSuccess) return cleanup(hip_fail(e, "hipEventCreate"));
+  }
   e = prepare_stage_kernels();
   if (e != hipSuccess) return cleanup(hip_fail(e, "hipFuncSetAttribute(dynamic LDS)"));
   {
@@ -520,8 +570,9 @@ int muon_init(const muon_matrix_desc* descs, int n, const muon_options* opts, vo
   // them so the staging can be released.
   std::vector<std::pair<const std::vector<Tile>*, size_t>> lists;
   lists.push_back({&p->tab.mom, p->lay.mom_tiles});
-  for (int prec = 0; prec < 2; ++prec)
-    for (int k = 0; k < 3; ++k) lists.push_back({&p->tab.ns[prec][k], p->lay.ns_tiles[prec][k]});
+  for (int grp = 0; grp < kGroups; ++grp)
+    for (int prec = 0; prec < 2; ++prec)
+      for (int k = 0; k < 3; ++k) lists.push_back({&p->tab.ns[grp][prec][k], p->lay.ns_tiles[grp][prec][k]});
   size_t tb = 0;
   for (auto& l : lists) tb += sizeof(Tile) * l.first->size();
   void* stage = nullptr;
@@ -622,19 +673,48 @@ int muon_step(muon_plan* p, const muon_matrix_desc* descs, int n, float a, float
     if ((rc = check_launch(launch_norm(mats, p->n, stream), "norm launch"))) return rc;
     if ((rc = prof_end(p, stream, pi))) return rc;
   }
-  for (int t = 1; t <= T; ++t) {
-    for (int k = 0; k < 3; ++k) {
-      for (int prec = 0; prec < 2; ++prec) {
-        const int ntab = (int)p->tab.ns[prec][k].size();
-        if (!ntab) continue;
-        StageArgs sa{mats, (const Tile*)(p->ws + p->lay.ns_tiles[prec][k]), ntab, t, T, p->opt.kmaster, a, b, c, lr};
-        // persistent grid: two blocks per CU, a multiple of 8 (every block
-        // keeps the XCD of the table entries it takes), never more than the table
-        const int slots = std::max(8, (2 * p->cus) / 8 * 8);
-        const int grid = std::min((ntab + 7) / 8 * 8, slots);
-        if ((rc = prof_begin(p, kKinds[k], stream, &pi))) return rc;
-        if ((rc = check_launch(launch_stage(k + 1, prec == 1, sa, grid, stream), kNames[k]))) return rc;
-        if ((rc = prof_end(p, stream, pi))) return rc;
+  if (T > 0) {
+    // The groups' iterations run on their own streams, forked from and joined
+    // back into the caller's stream (a single non-empty group stays on it).
+    bool busy[kGroups];
+    int ngroups = 0;
+    for (int grp = 0; grp < kGroups; ++grp) {
+      busy[grp] = false;
+      for (int prec = 0; prec < 2; ++prec) busy[grp] = busy[grp] || !p->tab.ns[grp][prec][kUpd].empty();
+      ngroups += busy[grp];
+    }
+    const bool fork = ngroups > 1;
+    hipError_t e = hipSuccess;
+    if (fork) {
+      e = hipEventRecord(p->fork_ev, stream);
+      for (int grp = 0; grp < kGroups && e == hipSuccess; ++grp)
+        if (busy[grp]) e = hipStreamWaitEvent(p->gs[grp], p->fork_ev, 0);
+      if (e != hipSuccess) return hip_fail(e, "fork of the group streams");
+    }
+    for (int grp = 0; grp < kGroups; ++grp) {
+      if (!busy[grp]) continue;
+      hipStream_t s = fork ? p->gs[grp] : stream;
+      for (int t = 1; t <= T; ++t) {
+        for (int k = 0; k < 3; ++k) {
+          for (int prec = 0; prec < 2; ++prec) {
+            const int ntab = (int)p->tab.ns[grp][prec][k].size();
+            if (!ntab) continue;
+            StageArgs sa{mats, (const Tile*)(p->ws + p->lay.ns_tiles[grp][prec][k]), ntab, t, T, p->opt.kmaster,
+                         a, b, c, lr};
+            // persistent grid: two blocks per CU, a multiple of 8 (every block
+            // keeps the XCD of the table entries it takes), never more than the table
+            const int slots = std::max(8, (2 * p->cus) / 8 * 8);
+            const int grid = std::min((ntab + 7) / 8 * 8, slots);
+            if ((rc = prof_begin(p, kKinds[k], s, &pi))) return rc;
+            if ((rc = check_launch(launch_stage(k + 1, prec == 1, sa, grid, s), kNames[k]))) return rc;
+            if ((rc = prof_end(p, s, pi))) return rc;
+          }
+        }
+      }
+      if (fork) {
+        e = hipEventRecord(p->join_ev[grp], s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(stream, p->join_ev[grp], 0);
+        if (e != hipSuccess) return hip_fail(e, "join of the group streams");
       }
     }
   }
@@ -650,6 +730,11 @@ int muon_destroy(muon_plan* p) {
     if (p->slot_ev[s]) (void)hipEventDestroy(p->slot_ev[s]);
   }
   if (p->last_ev) (void)hipEventDestroy(p->last_ev);
+  if (p->fork_ev) (void)hipEventDestroy(p->fork_ev);
+  for (int g = 0; g < kGroups; ++g) {
+    if (p->join_ev[g]) (void)hipEventDestroy(p->join_ev[g]);
+    if (p->gs[g]) (void)hipStreamDestroy(p->gs[g]);
+  }
   for (hipEvent_t ev : p->pev) (void)hipEventDestroy(ev);
   delete p;
   return MUON_OK;

@@ -86,7 +86,7 @@ def describe(shapes: Sequence[Tuple[int, int]], path: str = "bf16", x_master_ite
         tiles = [tuple(buf[3 * q:3 * q + 3]) for q in range(count.value)]
     d = dict(workspace_bytes=info.workspace_bytes, n_matrices=info.n_matrices, tile=info.tile,
              blocks=list(info.blocks), x_master_iters=info.x_master_iters, path=info.path,
-             n_f32_matrices=info.n_f32_matrices)
+             n_f32_matrices=info.n_f32_matrices, n_groups=info.n_groups)
     return d, tiles
 
 

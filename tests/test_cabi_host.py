@@ -105,7 +105,11 @@ def test_xcd_runs_are_balanced():
                 continue
             r, c = g.shapes[mat]
             load[b % 8] += max(r, c) if kind == _lib.KIND_GRAM else min(r, c)
-        assert max(load.values()) / min(load.values()) < 1.02
+        # each launch's table is cut into equal-cost runs at tile granularity:
+        # the XCD loads differ by at most one tile per launch (two groups)
+        tile_cost = max((max(r, c) if kind == _lib.KIND_GRAM else min(r, c)) for r, c in g.shapes)
+        assert max(load.values()) - min(load.values()) <= 2 * tile_cost
+        assert max(load.values()) / min(load.values()) < 1.03
         # each XCD works on a contiguous run of matrices: a matrix spans at most 2 XCDs
         xcds = {}
         for b, (mat, _, _) in enumerate(tiles):

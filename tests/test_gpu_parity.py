@@ -257,12 +257,20 @@ def test_profile_counts():
     M = [torch.zeros(s, device=dev) for s in shapes]
     G = [inputs.custom_gradient(r, c, 3).to(dev) for r, c in shapes]
     p = MuonStep(W, G, M)
+    from muon_newton_schulz_03_amd.muon import describe
+    groups = describe(shapes)[0]["n_groups"]
+    assert groups == 2  # two matrices: one per group stream
     p.profile(True)
     for _ in range(3):
         p.step(T=5)
     prof = p.read_profile()
-    assert prof["momentum"][1] == 3 and prof["gram"][1] == 15 and prof["update"][1] == 15
+    assert prof["momentum"][1] == 3 and prof["gram"][1] == 15 * groups and prof["update"][1] == 15 * groups
     assert all(prof[k][0] > 0 for k in ("momentum", "gram", "poly", "update"))
+    # only the selected kind is timed
+    p.profile(True, kinds=["update"])
+    p.step(T=5)
+    prof = p.read_profile()
+    assert prof["update"][1] == 5 * groups and prof["gram"][1] == 0 and prof["momentum"][1] == 0
     p.close()
 
 
