@@ -165,8 +165,8 @@ def main():
         if k in ("gram", "poly", "update"):
             per_kind[k]["tflops"] = wl.T * work[k] / (cnt / prof_steps) / (ms / cnt * 1e-3) / 1e12
     if "momentum" in per_kind:
-        per_kind["momentum"]["gbs"] = momentum_bytes(wl.shapes, True) / (per_kind["momentum"]["ms_per_launch"]
-                                                                          * 1e-3) / 1e9
+        mk = per_kind["momentum"]
+        mk["gbs"] = momentum_bytes(wl.shapes, True) / mk["launches_per_step"] / (mk["ms_per_launch"] * 1e-3) / 1e9
     dom = max(("gram", "poly", "update", "momentum"), key=lambda k: prof_all[k][0])
 
     # timed region: K steps; HIP events (recorded by the library on this stream)
@@ -191,7 +191,7 @@ def main():
     d_ms, d_cnt = prof[dom]
     d_launch_ms = d_ms / d_cnt
     if dom == "momentum":
-        achieved = momentum_bytes(wl.shapes, True) / (d_launch_ms * 1e-3) / 1e9
+        achieved = momentum_bytes(wl.shapes, True) / (d_cnt / args.steps) / (d_launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS}
     else:

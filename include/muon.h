@@ -163,10 +163,12 @@ typedef struct muon_plan_info {
   int32_t x_master_iters;
   int32_t path;
   int32_t n_f32_matrices;    /* matrices whose products run in fp32 (see below) */
-  int32_t n_groups;          /* matrix groups whose Newton-Schulz launches run on
-                                their own streams (1 or 2): a product kind has
-                                T * n_groups launches per step, plus one per
-                                group for each precision beyond the first */
+  int32_t n_groups;          /* matrix groups (contiguous, of equal cost) whose
+                                steps run on streams of their own, forked from
+                                and joined back into the caller's stream (1 or
+                                2): momentum and norm have n_groups launches per
+                                step, a product kind T * n_groups (times the
+                                precisions present) */
 } muon_plan_info;
 
 int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts,

@@ -117,7 +117,7 @@ struct Layout {
   };
   std::vector<M> m;
   size_t slots = 0, slot_bytes = 0;
-  size_t mom_tiles = 0;
+  size_t mom_tiles[kGroups] = {};
   size_t ns_tiles[kGroups][2][3] = {};
   size_t total = 0;
 };
@@ -146,8 +146,9 @@ Geometry geometry(const muon_matrix_desc& d, int path) {
 // since each launch runs one precision.
 enum { kGram = 0, kPoly = 1, kUpd = 2 };
 struct Tables {
-  std::vector<Tile> mom;
+  std::vector<Tile> mom[kGroups];       // [group]: momentum / apply tiles
   std::vector<Tile> ns[kGroups][2][3];  // [group][precision][kind]
+  int first[kGroups + 1] = {};          // group g holds matrices first[g] .. first[g+1]-1
 };
 
 // Tiles of one kind, ordered for the MI355X dispatcher, which places block b
@@ -228,9 +229,13 @@ Tables build_tables(const std::vector<Geometry>& geo) {
   }
   for (int i = 0; i < nm; ++i) {
     const Geometry& g = geo[i];
+    std::vector<Tile>& mom = t.mom[i < split ? 0 : 1];
     for (int a = 0; a < g.mp / kMomTile; ++a)
-      for (int b = 0; b < g.np / kMomTile; ++b) t.mom.push_back(Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0});
+      for (int b = 0; b < g.np / kMomTile; ++b) mom.push_back(Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0});
   }
+  t.first[0] = 0;
+  t.first[1] = split;
+  t.first[2] = nm;
   return t;
 }
 
@@ -240,8 +245,10 @@ size_t layout(const std::vector<Geometry>& geo, const Options& o, const Tables& 
   L->slot_bytes = align_up(sizeof(DevMat) * nm, kAlign);
   L->slots = off;
   off += L->slot_bytes * kSlots;
-  L->mom_tiles = off;
-  off = align_up(off + sizeof(Tile) * t.mom.size(), kAlign);
+  for (int grp = 0; grp < kGroups; ++grp) {
+    L->mom_tiles[grp] = off;
+    off = align_up(off + sizeof(Tile) * t.mom[grp].size(), kAlign);
+  }
   for (int grp = 0; grp < kGroups; ++grp)
     for (int prec = 0; prec < 2; ++prec)
       for (int k = 0; k < 3; ++k) {
@@ -463,11 +470,11 @@ int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts
     info->workspace_bytes = (int64_t)total;
     info->n_matrices = n;
     info->tile = kTile;
-    info->blocks[MUON_KIND_MOMENTUM] = (int32_t)t.mom.size();
+    info->blocks[MUON_KIND_MOMENTUM] = (int32_t)(t.mom[0].size() + t.mom[1].size());
     info->blocks[MUON_KIND_GRAM] = (int32_t)concat_tables(t, kGram).size();
     info->blocks[MUON_KIND_POLY] = (int32_t)concat_tables(t, kPoly).size();
     info->blocks[MUON_KIND_UPDATE] = (int32_t)concat_tables(t, kUpd).size();
-    info->blocks[MUON_KIND_APPLY] = (int32_t)t.mom.size();
+    info->blocks[MUON_KIND_APPLY] = info->blocks[MUON_KIND_MOMENTUM];
     info->blocks[MUON_KIND_NORM] = n;
     info->x_master_iters = o.kmaster;
     info->path = o.path;
@@ -475,14 +482,17 @@ int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts
     for (const Geometry& g : geo) nf += g.f32;
     info->n_f32_matrices = nf;
     int ng = 0;
-    for (int grp = 0; grp < kGroups; ++grp) ng += !t.ns[grp][0][kUpd].empty() || !t.ns[grp][1][kUpd].empty();
+    for (int grp = 0; grp < kGroups; ++grp) ng += !t.mom[grp].empty();
     info->n_groups = ng;
   }
   if (kind >= 0) {
     std::vector<Tile> v;
     switch (kind) {
       case MUON_KIND_MOMENTUM:
-      case MUON_KIND_APPLY: v = t.mom; break;
+      case MUON_KIND_APPLY:
+        v = t.mom[0];
+        v.insert(v.end(), t.mom[1].begin(), t.mom[1].end());
+        break;
       case MUON_KIND_GRAM:
       case MUON_KIND_POLY:
       case MUON_KIND_UPDATE: {
@@ -569,7 +579,7 @@ int muon_init(const muon_matrix_desc* descs, int n, const muon_options* opts, vo
   // Tile tables: staged through pinned memory, uploaded once; init waits for
   // them so the staging can be released.
   std::vector<std::pair<const std::vector<Tile>*, size_t>> lists;
-  lists.push_back({&p->tab.mom, p->lay.mom_tiles});
+  for (int grp = 0; grp < kGroups; ++grp) lists.push_back({&p->tab.mom[grp], p->lay.mom_tiles[grp]});
   for (int grp = 0; grp < kGroups; ++grp)
     for (int prec = 0; prec < 2; ++prec)
       for (int k = 0; k < 3; ++k) lists.push_back({&p->tab.ns[grp][prec][k], p->lay.ns_tiles[grp][prec][k]});
@@ -650,72 +660,70 @@ int muon_step(muon_plan* p, const muon_matrix_desc* descs, int n, float a, float
   }
 
   const DevMat* mats = slot_ptr(p, p->slot);
-  const Tile* mom_tiles = (const Tile*)(p->ws + p->lay.mom_tiles);
-  const int nmom = (int)p->tab.mom.size();
-
-  size_t pi = 0;
-  int rc;
-  MomArgs ma{mats, mom_tiles, momentum, nesterov ? 1 : 0};
-  if ((rc = prof_begin(p, MUON_KIND_MOMENTUM, stream, &pi))) return rc;
-  if ((rc = check_launch(launch_momentum(ma, nmom, stream), "momentum launch"))) return rc;
-  if ((rc = prof_end(p, stream, pi))) return rc;
-
-  if (T == 0) {
-    ApplyArgs aa{mats, mom_tiles, lr};
-    if ((rc = prof_begin(p, MUON_KIND_APPLY, stream, &pi))) return rc;
-    if ((rc = check_launch(launch_apply(aa, nmom, stream), "apply launch"))) return rc;
-    if ((rc = prof_end(p, stream, pi))) return rc;
-  }
   static const int kKinds[3] = {MUON_KIND_GRAM, MUON_KIND_POLY, MUON_KIND_UPDATE};
   static const char* kNames[3] = {"gram launch", "poly launch", "update launch"};
-  if (T > 0) {
-    if ((rc = prof_begin(p, MUON_KIND_NORM, stream, &pi))) return rc;
-    if ((rc = check_launch(launch_norm(mats, p->n, stream), "norm launch"))) return rc;
-    if ((rc = prof_end(p, stream, pi))) return rc;
+  size_t pi = 0;
+  int rc;
+
+  // Each group's whole step (momentum, norm, T iterations) runs on a stream of
+  // its own, forked from and joined back into the caller's stream (a single
+  // non-empty group stays on the caller's stream).  Starting group 1's
+  // momentum pass only after group 0's measured slower.
+  bool busy[kGroups];
+  int ngroups = 0;
+  for (int grp = 0; grp < kGroups; ++grp) {
+    busy[grp] = !p->tab.mom[grp].empty();
+    ngroups += busy[grp];
   }
-  if (T > 0) {
-    // The groups' iterations run on their own streams, forked from and joined
-    // back into the caller's stream (a single non-empty group stays on it).
-    bool busy[kGroups];
-    int ngroups = 0;
-    for (int grp = 0; grp < kGroups; ++grp) {
-      busy[grp] = false;
-      for (int prec = 0; prec < 2; ++prec) busy[grp] = busy[grp] || !p->tab.ns[grp][prec][kUpd].empty();
-      ngroups += busy[grp];
+  const bool fork = ngroups > 1;
+  hipError_t e = hipSuccess;
+  if (fork) {
+    e = hipEventRecord(p->fork_ev, stream);
+    for (int grp = 0; grp < kGroups && e == hipSuccess; ++grp)
+      if (busy[grp]) e = hipStreamWaitEvent(p->gs[grp], p->fork_ev, 0);
+    if (e != hipSuccess) return hip_fail(e, "fork of the group streams");
+  }
+  for (int grp = 0; grp < kGroups; ++grp) {
+    if (!busy[grp]) continue;
+    hipStream_t s = fork ? p->gs[grp] : stream;
+    const Tile* mom_tiles = (const Tile*)(p->ws + p->lay.mom_tiles[grp]);
+    const int nmom = (int)p->tab.mom[grp].size();
+    MomArgs ma{mats, mom_tiles, momentum, nesterov ? 1 : 0};
+    if ((rc = prof_begin(p, MUON_KIND_MOMENTUM, s, &pi))) return rc;
+    if ((rc = check_launch(launch_momentum(ma, nmom, s), "momentum launch"))) return rc;
+    if ((rc = prof_end(p, s, pi))) return rc;
+    if (T == 0) {
+      ApplyArgs aa{mats, mom_tiles, lr};
+      if ((rc = prof_begin(p, MUON_KIND_APPLY, s, &pi))) return rc;
+      if ((rc = check_launch(launch_apply(aa, nmom, s), "apply launch"))) return rc;
+      if ((rc = prof_end(p, s, pi))) return rc;
+    } else {
+      const int f0 = p->tab.first[grp], nf = p->tab.first[grp + 1] - f0;
+      if ((rc = prof_begin(p, MUON_KIND_NORM, s, &pi))) return rc;
+      if ((rc = check_launch(launch_norm(mats + f0, nf, s), "norm launch"))) return rc;
+      if ((rc = prof_end(p, s, pi))) return rc;
     }
-    const bool fork = ngroups > 1;
-    hipError_t e = hipSuccess;
-    if (fork) {
-      e = hipEventRecord(p->fork_ev, stream);
-      for (int grp = 0; grp < kGroups && e == hipSuccess; ++grp)
-        if (busy[grp]) e = hipStreamWaitEvent(p->gs[grp], p->fork_ev, 0);
-      if (e != hipSuccess) return hip_fail(e, "fork of the group streams");
-    }
-    for (int grp = 0; grp < kGroups; ++grp) {
-      if (!busy[grp]) continue;
-      hipStream_t s = fork ? p->gs[grp] : stream;
-      for (int t = 1; t <= T; ++t) {
-        for (int k = 0; k < 3; ++k) {
-          for (int prec = 0; prec < 2; ++prec) {
-            const int ntab = (int)p->tab.ns[grp][prec][k].size();
-            if (!ntab) continue;
-            StageArgs sa{mats, (const Tile*)(p->ws + p->lay.ns_tiles[grp][prec][k]), ntab, t, T, p->opt.kmaster,
-                         a, b, c, lr};
-            // persistent grid: two blocks per CU, a multiple of 8 (every block
-            // keeps the XCD of the table entries it takes), never more than the table
-            const int slots = std::max(8, (2 * p->cus) / 8 * 8);
-            const int grid = std::min((ntab + 7) / 8 * 8, slots);
-            if ((rc = prof_begin(p, kKinds[k], s, &pi))) return rc;
-            if ((rc = check_launch(launch_stage(k + 1, prec == 1, sa, grid, s), kNames[k]))) return rc;
-            if ((rc = prof_end(p, s, pi))) return rc;
-          }
+    for (int t = 1; t <= T; ++t) {
+      for (int k = 0; k < 3; ++k) {
+        for (int prec = 0; prec < 2; ++prec) {
+          const int ntab = (int)p->tab.ns[grp][prec][k].size();
+          if (!ntab) continue;
+          StageArgs sa{mats, (const Tile*)(p->ws + p->lay.ns_tiles[grp][prec][k]), ntab, t, T, p->opt.kmaster,
+                       a, b, c, lr};
+          // persistent grid: two blocks per CU, a multiple of 8 (every block
+          // keeps the XCD of the table entries it takes), never more than the table
+          const int slots = std::max(8, (2 * p->cus) / 8 * 8);
+          const int grid = std::min((ntab + 7) / 8 * 8, slots);
+          if ((rc = prof_begin(p, kKinds[k], s, &pi))) return rc;
+          if ((rc = check_launch(launch_stage(k + 1, prec == 1, sa, grid, s), kNames[k]))) return rc;
+          if ((rc = prof_end(p, s, pi))) return rc;
         }
       }
-      if (fork) {
-        e = hipEventRecord(p->join_ev[grp], s);
-        if (e == hipSuccess) e = hipStreamWaitEvent(stream, p->join_ev[grp], 0);
-        if (e != hipSuccess) return hip_fail(e, "join of the group streams");
-      }
+    }
+    if (fork) {
+      e = hipEventRecord(p->join_ev[grp], s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(stream, p->join_ev[grp], 0);
+      if (e != hipSuccess) return hip_fail(e, "join of the group streams");
     }
   }
   return note_slot_use(p, stream);

@@ -264,7 +264,7 @@ def test_profile_counts():
     for _ in range(3):
         p.step(T=5)
     prof = p.read_profile()
-    assert prof["momentum"][1] == 3 and prof["gram"][1] == 15 * groups and prof["update"][1] == 15 * groups
+    assert prof["momentum"][1] == 3 * groups and prof["gram"][1] == 15 * groups and prof["update"][1] == 15 * groups
     assert all(prof[k][0] > 0 for k in ("momentum", "gram", "poly", "update"))
     # only the selected kind is timed
     p.profile(True, kinds=["update"])
