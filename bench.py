@@ -200,7 +200,33 @@ def main():
                 "frac": achieved / PEAK_BF16_TFLOPS}
     roof["kernel"] = dom
     roof["ms_per_launch"] = d_launch_ms
+    roof["launches_per_step"] = d_cnt / args.steps
     roof["traffic"] = read_traffic(dom)
+    roof["note"] = ("the plan runs two matrix groups on two streams, so each launch covers half the set "
+                    "and shares the GPU with the other group's launches")
+
+    # The same kernel without the overlap: a one-stream plan, outside the timed region.
+    plan1 = MuonStep(W, grads[0], M, x_master_iters=args.x_master_iters, groups=1)
+    for t in range(2):
+        plan1.step(grads=grads[t], **kw)
+    plan1.profile(True, kinds=[dom])
+    plan1.read_profile()
+    one_steps = 10
+    for t in range(one_steps):
+        plan1.step(grads=grads[t % total], **kw)
+    torch.cuda.synchronize()
+    p1_ms, p1_cnt = plan1.read_profile()[dom]
+    plan1.close()
+    one_ms = p1_ms / p1_cnt
+    if dom == "momentum":
+        one_ach = momentum_bytes(wl.shapes, True) / (p1_cnt / one_steps) / (one_ms * 1e-3) / 1e9
+        one_peak = PEAK_HBM_GBS
+    else:
+        one_ach = wl.T * work[dom] / (p1_cnt / one_steps) / (one_ms * 1e-3) / 1e12
+        one_peak = PEAK_BF16_TFLOPS
+    roof_one = {"bound": roof["bound"], "achieved": one_ach, "peak": one_peak, "unit": roof["unit"],
+                "frac": one_ach / one_peak, "kernel": dom, "ms_per_launch": one_ms,
+                "note": f"one-stream plan (groups=1), {one_steps} steps after the timed region"}
 
     out = {
         "metric": "Muon steps/s on GPT-2-small hidden set (T=5); % bf16 MFMA peak",
@@ -225,6 +251,7 @@ def main():
         "kernels": per_kind,
         "kernels_pass": f"{prof_steps} steps after warm-up with every launch timed, outside the timed region",
         "roofline": roof,
+        "roofline_one_stream": roof_one,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)

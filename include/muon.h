@@ -93,13 +93,16 @@ typedef struct muon_matrix_desc {
 } muon_matrix_desc;
 
 /* Plan options.  NULL means: MUON_PATH_BF16, x_master_iters 3, no zeroing,
- * max_T 64. */
+ * max_T 64, 2 groups. */
 typedef struct muon_options {
   int32_t path;           /* MUON_PATH_BF16 or MUON_PATH_F32 */
   int32_t x_master_iters; /* bf16 path: iterations 1..k read X in a*X as a hi/lo
                              bf16 pair; < 0 selects the default 3; ignored on f32 */
   int32_t zero_momentum;  /* != 0: muon_init zeroes every momentum buffer */
   int32_t max_T;          /* largest T muon_step accepts; <= 0 selects 64 */
+  int32_t groups;         /* 1: every launch on the caller's stream; 2 (or <= 0,
+                             the default): two matrix groups, each on a stream of
+                             its own (see muon_plan_info.n_groups) */
 } muon_options;
 
 typedef struct muon_plan muon_plan;

@@ -36,7 +36,7 @@ class MatrixDesc(ctypes.Structure):
 
 class Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("x_master_iters", ctypes.c_int32),
-                ("zero_momentum", ctypes.c_int32), ("max_T", ctypes.c_int32)]
+                ("zero_momentum", ctypes.c_int32), ("max_T", ctypes.c_int32), ("groups", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):

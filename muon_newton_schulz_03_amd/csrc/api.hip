@@ -55,6 +55,7 @@ struct Options {
   int kmaster = 3;
   int zero = 0;
   int maxT = 64;
+  int groups = 2;
 };
 
 int read_options(const muon_options* o, Options* out) {
@@ -66,6 +67,8 @@ int read_options(const muon_options* o, Options* out) {
     r.kmaster = o->x_master_iters < 0 ? 3 : o->x_master_iters;
     r.zero = o->zero_momentum;
     r.maxT = o->max_T <= 0 ? 64 : o->max_T;
+    r.groups = o->groups <= 0 ? 2 : o->groups;
+    if (r.groups > 2) return fail(MUON_E_INVAL, "options.groups %d exceeds 2", r.groups);
     if (r.maxT > 4096) return fail(MUON_E_INVAL, "options.max_T %d exceeds 4096", r.maxT);
     if (r.kmaster > 4096) return fail(MUON_E_INVAL, "options.x_master_iters %d exceeds 4096", r.kmaster);
   }
@@ -187,9 +190,9 @@ std::vector<Tile> xcd_order(const std::vector<std::vector<Tile>>& per_mat, const
 
 // Matrices [0, split) form group 0 and [split, n) group 1, split where the
 // running Newton-Schulz cost is closest to half (a single matrix: group 1 is empty).
-int group_split(const std::vector<Geometry>& geo) {
+int group_split(const std::vector<Geometry>& geo, int groups) {
   const int nm = (int)geo.size();
-  if (nm < 2) return nm;
+  if (nm < 2 || groups < 2) return nm;
   std::vector<double> pre(nm + 1, 0.0);
   for (int i = 0; i < nm; ++i) {
     const double m = geo[i].mp, n = geo[i].np;
@@ -201,10 +204,10 @@ int group_split(const std::vector<Geometry>& geo) {
   return best;
 }
 
-Tables build_tables(const std::vector<Geometry>& geo) {
+Tables build_tables(const std::vector<Geometry>& geo, int groups) {
   Tables t;
   const int nm = (int)geo.size();
-  const int split = group_split(geo);
+  const int split = group_split(geo, groups);
   for (int grp = 0; grp < kGroups; ++grp)
   for (int prec = 0; prec < 2; ++prec) {
     std::vector<std::vector<Tile>> sym(nm), upd(nm);
@@ -434,7 +437,7 @@ size_t muon_workspace_size(const muon_matrix_desc* descs, int n, const muon_opti
   if (validate_all(descs, n, false)) return 0;
   std::vector<Geometry> geo(n);
   for (int i = 0; i < n; ++i) geo[i] = geometry(descs[i], o.path);
-  Tables t = build_tables(geo);
+  Tables t = build_tables(geo, o.groups);
   Layout L;
   return layout(geo, o, t, &L);
 }
@@ -463,7 +466,7 @@ int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts
   if (rc) return rc;
   std::vector<Geometry> geo(n);
   for (int i = 0; i < n; ++i) geo[i] = geometry(descs[i], o.path);
-  Tables t = build_tables(geo);
+  Tables t = build_tables(geo, o.groups);
   Layout L;
   const size_t total = layout(geo, o, t, &L);
   if (info) {
@@ -536,7 +539,7 @@ int muon_init(const muon_matrix_desc* descs, int n, const muon_options* opts, vo
   p->desc.assign(descs, descs + n);
   p->geo.resize(n);
   for (int i = 0; i < n; ++i) p->geo[i] = geometry(descs[i], o.path);
-  p->tab = build_tables(p->geo);
+  p->tab = build_tables(p->geo, o.groups);
   const size_t need = layout(p->geo, o, p->tab, &p->lay);
   if (ws_bytes < need) {
     delete p;

@@ -25,10 +25,10 @@ def version() -> str:
     return _lib.load().muon_version().decode()
 
 
-def _options(path: str, x_master_iters: int, zero_momentum: bool, max_T: int) -> Options:
+def _options(path: str, x_master_iters: int, zero_momentum: bool, max_T: int, groups: int = 0) -> Options:
     if path not in _PATHS:
         raise ValueError(f"path must be one of {sorted(_PATHS)}")
-    return Options(_PATHS[path], x_master_iters, int(zero_momentum), max_T)
+    return Options(_PATHS[path], x_master_iters, int(zero_momentum), max_T, groups)
 
 
 def _desc_array(shapes_dtypes, ptrs=None, scales=None) -> ctypes.Array:
@@ -68,11 +68,12 @@ def _tensor_descs(weights, grads, moms, scales) -> ctypes.Array:
 
 
 def describe(shapes: Sequence[Tuple[int, int]], path: str = "bf16", x_master_iters: int = -1,
-             kind: Optional[int] = None, grad_dtype=torch.bfloat16, weight_dtype=torch.float32) -> Tuple[dict, list]:
+             kind: Optional[int] = None, grad_dtype=torch.bfloat16, weight_dtype=torch.float32,
+             groups: int = 0) -> Tuple[dict, list]:
     """Host-only plan description (no GPU needed): sizes, grids and one tile list."""
     lib = _lib.load()
     arr = _desc_array([(r, c, _DTYPES[weight_dtype], _DTYPES[grad_dtype]) for r, c in shapes])
-    opts = _options(path, x_master_iters, False, 0)
+    opts = _options(path, x_master_iters, False, 0, groups)
     info = PlanInfo()
     count = ctypes.c_int32(0)
     k = -1 if kind is None else kind
@@ -100,7 +101,8 @@ class MuonStep:
 
     def __init__(self, weights: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
                  moms: Sequence[torch.Tensor], *, path: str = "bf16", x_master_iters: int = -1,
-                 zero_momentum: bool = False, max_T: int = 0, scales: Optional[Sequence[float]] = None):
+                 zero_momentum: bool = False, max_T: int = 0, scales: Optional[Sequence[float]] = None,
+                 groups: int = 0):
         self._lib = _lib.load()
         self.n = len(weights)
         if self.n == 0:
@@ -109,7 +111,7 @@ class MuonStep:
         self.scales = None if scales is None else list(scales)
         self._descs = _tensor_descs(weights, grads, moms, self.scales)
         self._keep = (list(weights), list(grads), list(moms))
-        self._opts = _options(path, x_master_iters, zero_momentum, max_T)
+        self._opts = _options(path, x_master_iters, zero_momentum, max_T, groups)
         ws = self._lib.muon_workspace_size(self._descs, self.n, ctypes.byref(self._opts))
         if ws == 0:
             raise _lib.MuonError(_lib.MUON_E_INVAL, _lib.last_error())

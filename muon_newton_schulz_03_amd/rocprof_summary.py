@@ -22,7 +22,8 @@ import sys
 from collections import defaultdict
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kernels.hip", "muon_internal.h")]
+# the kernels and the launch structure (api.hip decides which launches a step makes)
+KERNEL_SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kernels.hip", "muon_internal.h", "api.hip")]
 COPY_BYTES = 256 << 20  # bench.py --calibrate-copy: one plain copy of 256 MiB
 
 KINDS = {

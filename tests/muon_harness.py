@@ -33,7 +33,7 @@ class GpuRun:
 
 def run_gpu(shapes, grads_per_step, *, path="bf16", T=5, mu=0.95, nesterov=True, lr=0.05,
             coeffs=(A, B, C), w0=None, scales=None, x_master_iters=-1, sample=None, keep_steps=None,
-            weight_dtype=torch.float32, grads_on_device=False):
+            weight_dtype=torch.float32, grads_on_device=False, groups=0):
     """Run the HIP Muon step over the steps' gradients; return sampled W/M after each kept step.
 
     ``grads_per_step[t]`` is the list of gradients of step t (CPU or device tensors).
@@ -52,7 +52,7 @@ def run_gpu(shapes, grads_per_step, *, path="bf16", T=5, mu=0.95, nesterov=True,
         W = [w.to(dev, weight_dtype).contiguous() for w in w0]
     M = [torch.zeros(s, dtype=torch.float32, device=dev) for s in shapes]
     G = [g.to(dev).clone().contiguous() for g in grads_per_step[0]]  # own buffers
-    plan = MuonStep(W, G, M, path=path, x_master_iters=x_master_iters, scales=scales)
+    plan = MuonStep(W, G, M, path=path, x_master_iters=x_master_iters, scales=scales, groups=groups)
     out = GpuRun()
     for t, grads in enumerate(grads_per_step):
         if t > 0:

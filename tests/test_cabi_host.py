@@ -128,6 +128,25 @@ def test_short_matrices_take_fp32_products():
     assert {t[0] for t in tiles if t[0] >= 0} == {0, 1}
 
 
+def test_groups_option():
+    g = inputs.workload("gpt2_small")
+    d, _ = describe(g.shapes)
+    assert d["n_groups"] == 2
+    d, _ = describe(g.shapes, groups=1)
+    assert d["n_groups"] == 1
+    d, _ = describe([(768, 768)])
+    assert d["n_groups"] == 1  # one matrix: one group
+    # both groups of the default plan cover every matrix once, contiguously and by equal cost
+    d1, t1 = describe(g.shapes, kind=_lib.KIND_UPDATE, groups=1)
+    d2, t2 = describe(g.shapes, kind=_lib.KIND_UPDATE)
+    assert sorted(t for t in t1 if t[0] >= 0) == sorted(t for t in t2 if t[0] >= 0)
+    lib = _lib.load()
+    arr = descs([(64, 64)])
+    info = _lib.PlanInfo()
+    rc = lib.muon_describe(arr, 1, ctypes.byref(Options(0, -1, 0, 0, 3)), ctypes.byref(info), -1, None, 0, None)
+    assert rc == _lib.MUON_E_INVAL and "groups" in _lib.last_error()
+
+
 def test_master_iters_option():
     d, _ = describe([(64, 64)], x_master_iters=-1)
     assert d["x_master_iters"] == 3

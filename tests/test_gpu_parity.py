@@ -139,7 +139,8 @@ def test_width1024_fifty_steps():
 
 
 def test_determinism_and_grouping():
-    """Bitwise: two runs agree, and a grouped plan equals one plan per matrix."""
+    """Bitwise: two runs agree, a grouped plan equals one plan per matrix, and the
+    two-stream plan equals the one-stream plan."""
     say("[gpu] determinism / grouped launch")
     shapes = [(256, 384), (384, 256), (200, 200)]
     steps = [[inputs.custom_gradient(r, c, 500 + 10 * t + i) for i, (r, c) in enumerate(shapes)] for t in range(3)]
@@ -152,6 +153,10 @@ def test_determinism_and_grouping():
         single = run_gpu([shapes[i]], [[s[i]] for s in steps], lr=0.1)
         for t in range(3):
             assert torch.equal(single.W[t][0], g1.W[t][i])
+    one = run_gpu(shapes, steps, lr=0.1, groups=1)
+    for t in range(3):
+        for i in range(3):
+            assert torch.equal(one.W[t][i], g1.W[t][i]) and torch.equal(one.M[t][i], g1.M[t][i])
 
 
 def test_resume_equals_straight_run():
