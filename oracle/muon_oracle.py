@@ -107,12 +107,32 @@ def newton_schulz(X0: np.ndarray, a: float, b: float, c: float, T: int) -> np.nd
     return X
 
 
+def newton_schulz_schedule(X0: np.ndarray, schedule) -> np.ndarray:
+    """Newton-Schulz steps with their own polynomial each: step t uses schedule[t] = (a, b, c).
+
+    Speedrun overview page, paragraph "Reading guide": later records tune the
+    iteration's polynomials (Polar Express).  The pages give no values, so the
+    schedule is an argument; every step is the quintic step above with its own
+    (a, b, c).
+    """
+    X = np.asarray(X0, np.float64)
+    for a, b, c in schedule:
+        a, b, c = f32(a), f32(b), f32(c)
+        A = X @ X.T
+        B = b * A + c * (A @ A)
+        X = a * X + B @ X
+    return X
+
+
 def orthogonalise(U: np.ndarray, a: float, b: float, c: float, T: int,
-                  eps: float = EPS) -> Tuple[np.ndarray, float]:
-    """Short side first, normalise, iterate, and return O in U's orientation (and ||U||_F)."""
+                  eps: float = EPS, schedule=None) -> Tuple[np.ndarray, float]:
+    """Short side first, normalise, iterate, and return O in U's orientation (and ||U||_F).
+
+    ``schedule`` (a list of (a, b, c)) replaces a, b, c and T when given.
+    """
     X, transposed = to_short_side_first(np.asarray(U, np.float64))
     X0, nu = frobenius_normalise(X, eps)
-    X = newton_schulz(X0, a, b, c, T)
+    X = newton_schulz(X0, a, b, c, T) if schedule is None else newton_schulz_schedule(X0, schedule)
     return (X.T.copy() if transposed else X), nu
 
 
@@ -124,18 +144,19 @@ class StepResult:
     nu: float            # ||U||_F
 
 
-def muon_step(W: np.ndarray, G: np.ndarray, M: np.ndarray, *, a: float, b: float, c: float,
-              T: int, mu: float, nesterov: bool, lr: float, scale: float = 1.0,
-              eps: float = EPS) -> StepResult:
+def muon_step(W: np.ndarray, G: np.ndarray, M: np.ndarray, *, a: float = 0.0, b: float = 0.0, c: float = 0.0,
+              T: int = 0, mu: float, nesterov: bool, lr: float, scale: float = 1.0,
+              eps: float = EPS, schedule=None) -> StepResult:
     """One Muon step on one hidden matrix: momentum, orthogonalise, apply.
 
     W, G, M are the exact values the device sees (fp32 / bf16 / fp32).
     The weight step is W - lr*s*O in fp64; s <= 0 selects the default s = 1.
+    ``schedule`` (one (a, b, c) per iteration) replaces a, b, c and T when given.
     """
     G64 = as_f64(G)
     M_new = momentum_update(as_f64(M), G64, mu)
     U = nesterov_blend(G64, M_new, mu, nesterov)
-    O, nu = orthogonalise(U, a, b, c, T, eps)
+    O, nu = orthogonalise(U, a, b, c, T, eps, schedule=schedule)
     s = 1.0 if scale <= 0 else f32(scale)
     W_new = as_f64(W) - f32(lr) * s * O
     return StepResult(W_new, M_new, O, nu)

@@ -85,3 +85,22 @@ def test_momentum_mutants_fail_hand_example():
         m2 = mom(mom(np.zeros((4, 8), np.float32), g1, 0.5), g2, 0.5)
         ok = np.array_equal(m2, 0.5 * g1 + g2)
         assert ok == (mom is O.momentum_update)
+
+
+def test_schedule_mutants_fail_the_closed_form():
+    from test_oracle_pins import SCHEDULE, schedule_via_svd
+
+    def reversed_order(X0, schedule):
+        return O.newton_schulz_schedule(X0, list(schedule)[::-1])
+
+    def first_triple_only(X0, schedule):
+        return O.newton_schulz(X0, *schedule[0], len(schedule))
+
+    def pin(ns):
+        G = rng(41).standard_normal((30, 50))
+        X0, _ = O.frobenius_normalise(G)
+        return O.rel_frobenius(ns(X0, SCHEDULE), schedule_via_svd(X0, SCHEDULE)) < 1e-10
+
+    assert pin(O.newton_schulz_schedule)
+    assert not pin(reversed_order)
+    assert not pin(first_triple_only)

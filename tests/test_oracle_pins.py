@@ -348,3 +348,58 @@ def test_bf16_format_and_rounding():
     # the generators round through that same cast
     x = inputs.gaussian((64, 64), 0.02, 123, "cpu", torch.bfloat16)
     assert x.dtype == torch.bfloat16
+
+
+# --- P12: per-iteration coefficient schedules (overview page, "Reading guide":
+# later records tune the iteration's polynomials) -----------------------------
+
+SCHEDULE = [(A, B, C), (A, B, C), (3.0, -3.2, 1.2), (15 / 8, -10 / 8, 3 / 8), (1.5, -0.5, 0.0)]
+
+
+def schedule_via_svd(X0, schedule):
+    """Closed form: every step maps the singular values through its own scalar polynomial."""
+    U, S, Vt = np.linalg.svd(X0, full_matrices=False)
+    for a, b, c in schedule:
+        S = p_scalar(S, O.f32(a), O.f32(b), O.f32(c))
+    return (U * S) @ Vt
+
+
+@pytest.mark.parametrize("shape", [(40, 72), (72, 40), (9, 5)])
+def test_schedule_matches_svd_closed_form(shape):
+    G = rng(31).standard_normal(shape)
+    X, transposed = O.to_short_side_first(G)
+    X0, _ = O.frobenius_normalise(X)
+    got = O.newton_schulz_schedule(X0, SCHEDULE)
+    assert O.rel_frobenius(got, schedule_via_svd(X0, SCHEDULE)) < 1e-13
+    Ofull, _ = O.orthogonalise(G, 0, 0, 0, 0, schedule=SCHEDULE)
+    ref = schedule_via_svd(X0, SCHEDULE)
+    assert O.rel_frobenius(Ofull, ref.T if transposed else ref) < 1e-13
+
+
+def test_schedule_scalar_exact():
+    """1x1 input: the composition of the steps' scalar maps, in exact rational arithmetic."""
+    x = 0.375
+    got = O.newton_schulz_schedule(np.array([[x]]), SCHEDULE)[0, 0]
+    s = Fraction(x)
+    for a, b, c in SCHEDULE:
+        a, b, c = (Fraction(O.f32(v)) for v in (a, b, c))
+        s = a * s + b * s ** 3 + c * s ** 5
+    assert abs(got - float(s)) <= 1e-15 * max(1.0, abs(float(s)))
+
+
+def test_schedule_aggressive_then_convergent_reaches_polar():
+    """Three steps of the speedrun quintic put the singular values in its band; a
+    convergent quintic tail then reaches the polar factor."""
+    G = well_conditioned(48, 80, cond=5.0, seed=9)
+    sched = [(A, B, C)] * 3 + [(15 / 8, -10 / 8, 3 / 8)] * 8
+    out, _ = O.orthogonalise(G, 0, 0, 0, 0, schedule=sched)
+    assert O.rel_frobenius(out, polar(G)) < 1e-10
+    # the speedrun quintic alone does not get there
+    out5, _ = O.orthogonalise(G, A, B, C, 5)
+    assert O.rel_frobenius(out5, polar(G)) > 0.05
+
+
+def test_schedule_of_one_triple_is_the_plain_iteration():
+    G = rng(33).standard_normal((24, 40))
+    X0, _ = O.frobenius_normalise(G)
+    assert np.array_equal(O.newton_schulz_schedule(X0, [(A, B, C)] * 5), O.newton_schulz(X0, A, B, C, 5))
