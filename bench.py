@@ -183,6 +183,20 @@ def main():
     ms_total = start.elapsed_time(stop)
     prof = plan.read_profile()
     plan.profile(False)
+
+    # Per-iteration coefficient schedule (muon_step_schedule), outside the timed
+    # region: the speedrun quintic for 3 iterations, then a convergent quintic.
+    sched = [wl.coeffs] * 3 + [(15 / 8, -10 / 8, 3 / 8)] * 2
+    sched_steps = 20
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    plan.step(grads=grads[0], schedule=sched, momentum=wl.momentum, nesterov=wl.nesterov, lr=wl.lr)
+    torch.cuda.synchronize()
+    ev0.record()
+    for t in range(sched_steps):
+        plan.step(grads=grads[t % total], schedule=sched, momentum=wl.momentum, nesterov=wl.nesterov, lr=wl.lr)
+    ev1.record()
+    torch.cuda.synchronize()
+    sched_ms = ev0.elapsed_time(ev1) / sched_steps
     plan.close()
 
     ms_step = ms_total / args.steps
@@ -252,6 +266,8 @@ def main():
         "kernels_pass": f"{prof_steps} steps after warm-up with every launch timed, outside the timed region",
         "roofline": roof,
         "roofline_one_stream": roof_one,
+        "schedule": {"coeffs": [list(t) for t in sched], "ms_per_step": sched_ms, "steps_per_s": 1000.0 / sched_ms,
+                     "note": f"muon_step_schedule, {sched_steps} steps after the timed region"},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)

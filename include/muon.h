@@ -122,16 +122,29 @@ size_t muon_workspace_size(const muon_matrix_desc* descs, int n, const muon_opti
 int muon_init(const muon_matrix_desc* descs, int n, const muon_options* opts,
               void* workspace, size_t ws_bytes, void* hip_stream, muon_plan** out_plan);
 
-/* Enqueue one Muon step over every matrix of the plan on hip_stream:
- * 1 momentum launch and 1 norm launch, then 3 launches per Newton-Schulz iteration (all
- * matrices of one precision grouped in each launch: 6 per iteration when the
- * plan mixes bf16 and fp32 matrices); T == 0 enqueues one weight-step launch
- * instead (W <- W - lr*s*X0).  descs == NULL reuses the pointers the plan
- * holds; otherwise n must equal the plan's count and shapes, dtypes and
- * scales must match (pointers may differ).  Requirements: 0 <= T <= max_T,
+/* Enqueue one Muon step over every matrix of the plan on hip_stream.  Per
+ * matrix group (muon_plan_info.n_groups; each group on a stream of its own,
+ * forked from and joined back into hip_stream, so later work on hip_stream
+ * sees the whole step): 1 momentum launch and 1 norm launch, then 3 launches
+ * per Newton-Schulz iteration (all matrices of one precision grouped in each
+ * launch: 6 per iteration when the group mixes bf16 and fp32 matrices); T == 0
+ * enqueues one weight-step launch instead of norm and iterations
+ * (W <- W - lr*s*X0).  descs == NULL reuses the pointers the plan holds;
+ * otherwise n must equal the plan's count and shapes, dtypes and scales must
+ * match (pointers may differ).  Requirements: 0 <= T <= max_T,
  * 0 <= momentum <= 1, a, b, c, lr finite. */
 int muon_step(muon_plan* plan, const muon_matrix_desc* descs, int n, float a, float b, float c,
               int T, float momentum, int nesterov, float lr, void* hip_stream);
+
+/* muon_step with a polynomial of its own for every iteration: iteration t
+ * (1-based) uses a = coeffs[3(t-1)], b = coeffs[3(t-1)+1], c = coeffs[3(t-1)+2].
+ * The speedrun overview page ("The NanoGPT speedrun", paragraph "Reading
+ * guide") names later records that tune the iteration's polynomials (Polar
+ * Express); it gives no values, so the schedule is the caller's.  coeffs is a
+ * host array of 3*T finite floats, read during the call (the caller may reuse
+ * it on return); NULL is allowed only with T == 0. */
+int muon_step_schedule(muon_plan* plan, const muon_matrix_desc* descs, int n, const float* coeffs, int T,
+                       float momentum, int nesterov, float lr, void* hip_stream);
 
 /* Free the plan's host state.  The workspace stays the caller's. */
 int muon_destroy(muon_plan* plan);

@@ -23,7 +23,7 @@ KIND_MOMENTUM, KIND_GRAM, KIND_POLY, KIND_UPDATE, KIND_APPLY, KIND_NORM = range(
 KIND_COUNT = 6
 KIND_NAMES = ("momentum", "gram", "poly", "update", "apply", "norm")
 
-EXPORTS = ("muon_version", "muon_workspace_size", "muon_init", "muon_step", "muon_destroy",
+EXPORTS = ("muon_version", "muon_workspace_size", "muon_init", "muon_step", "muon_step_schedule", "muon_destroy",
            "muon_last_error", "muon_describe", "muon_profile_enable", "muon_profile_select", "muon_profile_read")
 
 
@@ -81,6 +81,9 @@ def load(path: str = None) -> ctypes.CDLL:
     lib.muon_step.argtypes = [ctypes.c_void_p, P(MatrixDesc), ctypes.c_int, ctypes.c_float, ctypes.c_float,
                               ctypes.c_float, ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_float,
                               ctypes.c_void_p]
+    lib.muon_step_schedule.restype = ctypes.c_int
+    lib.muon_step_schedule.argtypes = [ctypes.c_void_p, P(MatrixDesc), ctypes.c_int, P(ctypes.c_float), ctypes.c_int,
+                                       ctypes.c_float, ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
     lib.muon_destroy.restype = ctypes.c_int
     lib.muon_destroy.argtypes = [ctypes.c_void_p]
     lib.muon_describe.restype = ctypes.c_int

@@ -627,13 +627,19 @@ int muon_init(const muon_matrix_desc* descs, int n, const muon_options* opts, vo
   return MUON_OK;
 }
 
-int muon_step(muon_plan* p, const muon_matrix_desc* descs, int n, float a, float b, float c, int T, float momentum,
-              int nesterov, float lr, void* hip_stream) {
+// One step; iteration t uses sched[3(t-1) .. 3(t-1)+2] when sched is given, else (a, b, c).
+static int step_impl(muon_plan* p, const muon_matrix_desc* descs, int n, const float* sched, float a, float b,
+                     float c, int T, float momentum, int nesterov, float lr, void* hip_stream) {
   g_err.clear();
   if (!p) return fail(MUON_E_INVAL, "plan is NULL");
   if (T < 0 || T > p->opt.maxT) return fail(MUON_E_INVAL, "T=%d outside [0, max_T=%d]", T, p->opt.maxT);
-  if (!std::isfinite(a) || !std::isfinite(b) || !std::isfinite(c) || !std::isfinite(lr))
-    return fail(MUON_E_INVAL, "a, b, c and lr must be finite");
+  if (sched) {
+    for (int q = 0; q < 3 * T; ++q)
+      if (!std::isfinite(sched[q])) return fail(MUON_E_INVAL, "schedule entry %d (iteration %d) is not finite", q, q / 3 + 1);
+  } else if (!std::isfinite(a) || !std::isfinite(b) || !std::isfinite(c)) {
+    return fail(MUON_E_INVAL, "a, b and c must be finite");
+  }
+  if (!std::isfinite(lr)) return fail(MUON_E_INVAL, "lr must be finite");
   if (!(momentum >= 0.f && momentum <= 1.f)) return fail(MUON_E_INVAL, "momentum %g outside [0, 1]", momentum);
   hipStream_t stream = (hipStream_t)hip_stream;
 
@@ -711,8 +717,9 @@ int muon_step(muon_plan* p, const muon_matrix_desc* descs, int n, float a, float
         for (int prec = 0; prec < 2; ++prec) {
           const int ntab = (int)p->tab.ns[grp][prec][k].size();
           if (!ntab) continue;
+          const float* tc = sched ? sched + 3 * (t - 1) : nullptr;
           StageArgs sa{mats, (const Tile*)(p->ws + p->lay.ns_tiles[grp][prec][k]), ntab, t, T, p->opt.kmaster,
-                       a, b, c, lr};
+                       tc ? tc[0] : a, tc ? tc[1] : b, tc ? tc[2] : c, lr};
           // persistent grid: two blocks per CU, a multiple of 8 (every block
           // keeps the XCD of the table entries it takes), never more than the table
           const int slots = std::max(8, (2 * p->cus) / 8 * 8);
@@ -730,6 +737,20 @@ int muon_step(muon_plan* p, const muon_matrix_desc* descs, int n, float a, float
     }
   }
   return note_slot_use(p, stream);
+}
+
+int muon_step(muon_plan* p, const muon_matrix_desc* descs, int n, float a, float b, float c, int T, float momentum,
+              int nesterov, float lr, void* hip_stream) {
+  return step_impl(p, descs, n, nullptr, a, b, c, T, momentum, nesterov, lr, hip_stream);
+}
+
+int muon_step_schedule(muon_plan* p, const muon_matrix_desc* descs, int n, const float* coeffs, int T,
+                       float momentum, int nesterov, float lr, void* hip_stream) {
+  if (!coeffs && T > 0) {
+    g_err.clear();
+    return fail(MUON_E_INVAL, "coeffs is NULL with T=%d", T);
+  }
+  return step_impl(p, descs, n, coeffs, 0.f, 0.f, 0.f, T, momentum, nesterov, lr, hip_stream);
 }
 
 int muon_destroy(muon_plan* p) {

@@ -128,8 +128,12 @@ class MuonStep:
 
     def step(self, *, a: float = DEFAULT_COEFFS[0], b: float = DEFAULT_COEFFS[1], c: float = DEFAULT_COEFFS[2],
              T: int = 5, momentum: float = 0.95, nesterov: bool = True, lr: float = 0.05,
-             weights=None, grads=None, moms=None) -> None:
-        """Enqueue one step.  New tensors (same shapes/dtypes) may replace any of the lists."""
+             weights=None, grads=None, moms=None, schedule: Optional[Sequence[Tuple[float, float, float]]] = None
+             ) -> None:
+        """Enqueue one step.  New tensors (same shapes/dtypes) may replace any of the lists.
+
+        ``schedule`` (one (a, b, c) per iteration) replaces a, b, c and T.
+        """
         descs = None
         if weights is not None or grads is not None or moms is not None:
             w, g, m = self._keep
@@ -139,6 +143,14 @@ class MuonStep:
             descs = _tensor_descs(w, g, m, self.scales)
             self._keep = (w, g, m)
         stream = torch.cuda.current_stream(self.device).cuda_stream
+        if schedule is not None:
+            flat = [float(v) for triple in schedule for v in triple]
+            if len(flat) != 3 * len(schedule):
+                raise ValueError("schedule entries must be (a, b, c) triples")
+            arr = (ctypes.c_float * max(len(flat), 1))(*flat)
+            _lib.check(self._lib.muon_step_schedule(self._plan, descs, self.n, arr, len(schedule), momentum,
+                                                    int(bool(nesterov)), lr, ctypes.c_void_p(stream)))
+            return
         _lib.check(self._lib.muon_step(self._plan, descs, self.n, a, b, c, int(T), momentum, int(bool(nesterov)),
                                        lr, ctypes.c_void_p(stream)))
 

@@ -33,7 +33,7 @@ class GpuRun:
 
 def run_gpu(shapes, grads_per_step, *, path="bf16", T=5, mu=0.95, nesterov=True, lr=0.05,
             coeffs=(A, B, C), w0=None, scales=None, x_master_iters=-1, sample=None, keep_steps=None,
-            weight_dtype=torch.float32, grads_on_device=False, groups=0):
+            weight_dtype=torch.float32, grads_on_device=False, groups=0, schedule=None):
     """Run the HIP Muon step over the steps' gradients; return sampled W/M after each kept step.
 
     ``grads_per_step[t]`` is the list of gradients of step t (CPU or device tensors).
@@ -58,7 +58,10 @@ def run_gpu(shapes, grads_per_step, *, path="bf16", T=5, mu=0.95, nesterov=True,
         if t > 0:
             for i in range(n):
                 G[i].copy_(grads[i].to(dev), non_blocking=False)
-        plan.step(a=coeffs[0], b=coeffs[1], c=coeffs[2], T=T, momentum=mu, nesterov=nesterov, lr=lr)
+        if schedule is not None:
+            plan.step(schedule=schedule, momentum=mu, nesterov=nesterov, lr=lr)
+        else:
+            plan.step(a=coeffs[0], b=coeffs[1], c=coeffs[2], T=T, momentum=mu, nesterov=nesterov, lr=lr)
         if t in keep:
             torch.cuda.synchronize()
             out.W.append([W[i].to("cpu", torch.float64).clone() for i in sample])
@@ -72,7 +75,7 @@ def run_gpu(shapes, grads_per_step, *, path="bf16", T=5, mu=0.95, nesterov=True,
 
 
 def oracle_steps(w0, grads, *, T=5, mu=0.95, nesterov=True, lr=0.05, coeffs=(A, B, C), scale=1.0,
-                 need_ns=None):
+                 need_ns=None, schedule=None):
     """Oracle over one matrix's step sequence.  ``need_ns``: the steps whose O is
     needed; the others only advance the momentum, and W is then not tracked
     (reported as None)."""
@@ -84,7 +87,7 @@ def oracle_steps(w0, grads, *, T=5, mu=0.95, nesterov=True, lr=0.05, coeffs=(A, 
         G = O.as_f64(g)
         if need_ns is None or t in need_ns:
             r = O.muon_step(W if W is not None else np.zeros(G.shape), G, M, a=a, b=b, c=c, T=T, mu=mu,
-                            nesterov=nesterov, lr=lr, scale=scale)
+                            nesterov=nesterov, lr=lr, scale=scale, schedule=schedule)
             M = r.M
             W = r.W if W is not None else None
             res.append(O.StepResult(W, M, r.O, r.nu))

@@ -209,8 +209,14 @@ def test_validation_errors(lib):
 def test_step_and_destroy_on_null_plan(lib):
     expect_error(_lib.MUON_E_INVAL, lib.muon_step, None, None, 0, 1.0, 1.0, 1.0, 5, 0.9, 1, 0.1, None,
                  match="plan")
+    coeffs = (ctypes.c_float * 6)(3.4445, -4.775, 2.0315, 3.4445, -4.775, 2.0315)
+    expect_error(_lib.MUON_E_INVAL, lib.muon_step_schedule, None, None, 0, coeffs, 2, 0.9, 1, 0.1, None,
+                 match="NULL")
+    expect_error(_lib.MUON_E_INVAL, lib.muon_step_schedule, None, None, 0, None, 2, 0.9, 1, 0.1, None,
+                 match="coeffs is NULL")
     assert lib.muon_destroy(None) == 0
     expect_error(_lib.MUON_E_INVAL, lib.muon_profile_enable, None, 1)
+    expect_error(_lib.MUON_E_INVAL, lib.muon_profile_select, None, 1)
     expect_error(_lib.MUON_E_INVAL, lib.muon_profile_read, None, None, None)
     # errors are per thread and cleared by the next successful call
     assert lib.muon_destroy(None) == 0 and _lib.last_error() == ""

@@ -20,7 +20,7 @@ RAGGED = [(4, 8), (8, 4), (1, 1), (1, 300), (300, 1), (130, 130), (200, 333), (3
 
 
 def compare_run(shapes, grads_steps, gpu, *, path, lr, mu, nesterov, T=5, coeffs=(A, B, C), w0=None,
-                scales=None, sample=None, steps=None, tol=None):
+                scales=None, sample=None, steps=None, tol=None, schedule=None):
     tol = tol if tol is not None else (TOL_F32 if path == "f32" else TOL_BF16)
     sample = list(range(len(shapes))) if sample is None else list(sample)
     worst = 0.0
@@ -28,7 +28,7 @@ def compare_run(shapes, grads_steps, gpu, *, path, lr, mu, nesterov, T=5, coeffs
         wi0 = w0[i] if w0 is not None else torch.zeros(shapes[i])
         s = 1.0 if scales is None or scales[i] <= 0 else O.f32(scales[i])
         ref = oracle_steps(wi0, [g[i] for g in grads_steps], T=T, mu=mu, nesterov=nesterov, lr=lr,
-                           coeffs=coeffs, scale=s)
+                           coeffs=coeffs, scale=s, schedule=schedule)
         prev = O.as_f64(wi0)
         for t, r in enumerate(ref):
             if gpu.W[t] is None or (t > 0 and gpu.W[t - 1] is None):
@@ -288,3 +288,32 @@ def test_master_copy_settings(k):
     gpu = run_gpu(shapes, steps, lr=1.0, x_master_iters=k)
     worst = compare_run(shapes, steps, gpu, path="bf16", lr=1.0, mu=0.95, nesterov=True)
     say(f"  worst rel err {worst:.3e}")
+
+
+# per-iteration coefficient schedules (muon_step_schedule): an aggressive start
+# with the speedrun quintic, then other polynomials, a convergent quintic last
+SCHED5 = [(A, B, C), (A, B, C), (3.0, -3.2, 1.2), (15 / 8, -10 / 8, 3 / 8), (1.5, -0.5, 0.0)]
+SCHED8 = [(A, B, C)] * 3 + [(15 / 8, -10 / 8, 3 / 8)] * 5
+
+
+@pytest.mark.parametrize("path,sched", [("bf16", SCHED5), ("bf16", SCHED8), ("f32", SCHED5)])
+def test_schedule_parity(path, sched):
+    say(f"[gpu] schedule path={path} T={len(sched)}")
+    gdt = torch.float32 if path == "f32" else torch.bfloat16
+    shapes = [(256, 384), (384, 256), (768, 768), (100, 37)]
+    steps = [[inputs.custom_gradient(r, c, 700 + 10 * t + i, gdt, std=0.02) for i, (r, c) in enumerate(shapes)]
+             for t in range(2)]
+    gpu = run_gpu(shapes, steps, path=path, lr=0.5, schedule=sched)
+    worst = compare_run(shapes, steps, gpu, path=path, lr=0.5, mu=0.95, nesterov=True, schedule=sched)
+    say(f"  worst rel err {worst:.3e}")
+
+
+def test_schedule_of_one_triple_equals_plain_step():
+    say("[gpu] uniform schedule == muon_step")
+    shapes = [(256, 512), (512, 256)]
+    steps = [[inputs.custom_gradient(r, c, 800 + 10 * t + i) for i, (r, c) in enumerate(shapes)] for t in range(2)]
+    plain = run_gpu(shapes, steps, lr=0.1)
+    sched = run_gpu(shapes, steps, lr=0.1, schedule=[(A, B, C)] * 5)
+    for t in range(2):
+        for i in range(2):
+            assert torch.equal(plain.W[t][i], sched.W[t][i]) and torch.equal(plain.M[t][i], sched.M[t][i])
