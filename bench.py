@@ -197,6 +197,26 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     sched_ms = ev0.elapsed_time(ev1) / sched_steps
+
+    # The step captured once in a HIP graph and replayed (fixed gradient buffers,
+    # as when a training loop writes its gradients in place), outside the timed region.
+    gbuf = [g.clone() for g in grads[0]]
+    plan.step(grads=gbuf, **kw)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan.step(**kw)
+    torch.cuda.synchronize()
+    graph_steps = 50
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(graph_steps):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    graph_ms = ev0.elapsed_time(ev1) / graph_steps
+    del graph
     plan.close()
 
     ms_step = ms_total / args.steps
@@ -268,6 +288,8 @@ def main():
         "roofline_one_stream": roof_one,
         "schedule": {"coeffs": [list(t) for t in sched], "ms_per_step": sched_ms, "steps_per_s": 1000.0 / sched_ms,
                      "note": f"muon_step_schedule, {sched_steps} steps after the timed region"},
+        "graph": {"ms_per_step": graph_ms, "steps_per_s": 1000.0 / graph_ms,
+                  "note": f"one step captured in a HIP graph, {graph_steps} replays after the timed region"},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)

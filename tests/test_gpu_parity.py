@@ -317,3 +317,42 @@ def test_schedule_of_one_triple_equals_plain_step():
     for t in range(2):
         for i in range(2):
             assert torch.equal(plain.W[t][i], sched.W[t][i]) and torch.equal(plain.M[t][i], sched.M[t][i])
+
+
+@pytest.mark.parametrize("groups", [1, 2])
+def test_graph_capture_replays_match_eager(groups):
+    """A step captured in a graph (descriptors unchanged, profiling off), replayed
+    several times with eager work and synchronisation in between, gives the eager
+    run's weights and momentum bitwise after every replay."""
+    say(f"[gpu] graph capture groups={groups}")
+    from muon_newton_schulz_03_amd import MuonStep
+    dev = "cuda:0"
+    shapes = [(256, 384), (384, 256), (128, 640)]
+    G = [inputs.custom_gradient(r, c, 950 + i).to(dev) for i, (r, c) in enumerate(shapes)]
+    kw = dict(T=5, momentum=0.95, nesterov=True, lr=0.1)
+
+    We = [torch.zeros(s, device=dev) for s in shapes]
+    Me = [torch.zeros(s, device=dev) for s in shapes]
+    pe = MuonStep(We, G, Me, groups=groups)
+    Wg = [torch.zeros(s, device=dev) for s in shapes]
+    Mg = [torch.zeros(s, device=dev) for s in shapes]
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        pg = MuonStep(Wg, G, Mg, groups=groups)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pg.step(**kw)  # captured, not run
+    torch.cuda.synchronize()
+    for w in Wg + Mg:
+        assert torch.count_nonzero(w).item() == 0  # capture ran nothing
+    for rep in range(4):
+        pe.step(**kw)
+        graph.replay()
+        scratch = torch.randn(1 << 20, device=dev).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        for i in range(len(shapes)):
+            assert torch.equal(We[i], Wg[i]) and torch.equal(Me[i], Mg[i]), f"replay {rep} matrix {i}"
+        assert torch.isfinite(scratch)
+    pe.close()
+    pg.close()
