@@ -105,12 +105,88 @@ def cpu_baseline(wl, budget_s: float = 12.0):
                       f"in {el:.1f} s, scaled by 12 layers"}
 
 
+def after_timed_region(args, plan, grads, total, kw, wl, W, M, work, dom):
+    """Measurements after the timed region: the dominant kernel in a one-stream plan,
+    a per-iteration coefficient schedule, and the step replayed from a HIP graph."""
+    import torch
+
+    from muon_newton_schulz_03_amd import MuonStep
+
+    # Per-iteration coefficient schedule (muon_step_schedule): the speedrun
+    # quintic for 3 iterations, then a convergent quintic.
+    sched = [wl.coeffs] * 3 + [(15 / 8, -10 / 8, 3 / 8)] * 2
+    sched_steps = 20
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    plan.step(grads=grads[0], schedule=sched, momentum=wl.momentum, nesterov=wl.nesterov, lr=wl.lr)
+    torch.cuda.synchronize()
+    ev0.record()
+    for t in range(sched_steps):
+        plan.step(grads=grads[t % total], schedule=sched, momentum=wl.momentum, nesterov=wl.nesterov, lr=wl.lr)
+    ev1.record()
+    torch.cuda.synchronize()
+    sched_ms = ev0.elapsed_time(ev1) / sched_steps
+
+    # The step captured once in a HIP graph and replayed (fixed gradient buffers,
+    # as when a training loop writes its gradients in place), outside the timed region.
+    gbuf = [g.clone() for g in grads[0]]
+    plan.step(grads=gbuf, **kw)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan.step(**kw)
+    torch.cuda.synchronize()
+    graph_steps = 50
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(graph_steps):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    graph_ms = ev0.elapsed_time(ev1) / graph_steps
+    del graph
+
+    # The same kernel without the overlap: a one-stream plan, outside the timed region.
+    plan1 = MuonStep(W, grads[0], M, x_master_iters=args.x_master_iters, groups=1)
+    for t in range(2):
+        plan1.step(grads=grads[t], **kw)
+    plan1.profile(True, kinds=[dom])
+    plan1.read_profile()
+    one_steps = 10
+    for t in range(one_steps):
+        plan1.step(grads=grads[t % total], **kw)
+    torch.cuda.synchronize()
+    p1_ms, p1_cnt = plan1.read_profile()[dom]
+    plan1.close()
+    one_ms = p1_ms / p1_cnt
+    if dom == "momentum":
+        one_ach = momentum_bytes(wl.shapes, True) / (p1_cnt / one_steps) / (one_ms * 1e-3) / 1e9
+        one_peak = PEAK_HBM_GBS
+    else:
+        one_ach = wl.T * work[dom] / (p1_cnt / one_steps) / (one_ms * 1e-3) / 1e12
+        one_peak = PEAK_BF16_TFLOPS
+    roof_one = {"bound": "hbm" if dom == "momentum" else "mfma", "achieved": one_ach, "peak": one_peak,
+                "unit": "GB/s" if dom == "momentum" else "TFLOP/s",
+                "frac": one_ach / one_peak, "kernel": dom, "ms_per_launch": one_ms,
+                "note": f"one-stream plan (groups=1), {one_steps} steps after the timed region"}
+
+    return {
+        "roofline_one_stream": roof_one,
+        "schedule": {"coeffs": [list(t) for t in sched], "ms_per_step": sched_ms, "steps_per_s": 1000.0 / sched_ms,
+                     "note": f"muon_step_schedule, {sched_steps} steps after the timed region"},
+        "graph": {"ms_per_step": graph_ms, "steps_per_s": 1000.0 / graph_ms,
+                  "note": f"one step captured in a HIP graph, {graph_steps} replays after the timed region"},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the passes after the timed region (one-stream roofline, schedule, graph)")
     ap.add_argument("--x-master-iters", type=int, default=-1)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 256 MiB device copy first (counter calibration)")
@@ -184,41 +260,10 @@ def main():
     prof = plan.read_profile()
     plan.profile(False)
 
-    # Per-iteration coefficient schedule (muon_step_schedule), outside the timed
-    # region: the speedrun quintic for 3 iterations, then a convergent quintic.
-    sched = [wl.coeffs] * 3 + [(15 / 8, -10 / 8, 3 / 8)] * 2
-    sched_steps = 20
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    plan.step(grads=grads[0], schedule=sched, momentum=wl.momentum, nesterov=wl.nesterov, lr=wl.lr)
-    torch.cuda.synchronize()
-    ev0.record()
-    for t in range(sched_steps):
-        plan.step(grads=grads[t % total], schedule=sched, momentum=wl.momentum, nesterov=wl.nesterov, lr=wl.lr)
-    ev1.record()
-    torch.cuda.synchronize()
-    sched_ms = ev0.elapsed_time(ev1) / sched_steps
-
-    # The step captured once in a HIP graph and replayed (fixed gradient buffers,
-    # as when a training loop writes its gradients in place), outside the timed region.
-    gbuf = [g.clone() for g in grads[0]]
-    plan.step(grads=gbuf, **kw)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        plan.step(**kw)
-    torch.cuda.synchronize()
-    graph_steps = 50
-    graph.replay()
-    torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(graph_steps):
-        graph.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    graph_ms = ev0.elapsed_time(ev1) / graph_steps
-    del graph
+    extras = {}
+    if not args.no_extras:
+        extras = after_timed_region(args, plan, grads, total, kw, wl, W, M, work, dom)
     plan.close()
-
     ms_step = ms_total / args.steps
     steps_per_s = 1000.0 / ms_step
     tflops = work["step"] * steps_per_s / 1e12
@@ -238,29 +283,6 @@ def main():
     roof["traffic"] = read_traffic(dom)
     roof["note"] = ("the plan runs two matrix groups on two streams, so each launch covers half the set "
                     "and shares the GPU with the other group's launches")
-
-    # The same kernel without the overlap: a one-stream plan, outside the timed region.
-    plan1 = MuonStep(W, grads[0], M, x_master_iters=args.x_master_iters, groups=1)
-    for t in range(2):
-        plan1.step(grads=grads[t], **kw)
-    plan1.profile(True, kinds=[dom])
-    plan1.read_profile()
-    one_steps = 10
-    for t in range(one_steps):
-        plan1.step(grads=grads[t % total], **kw)
-    torch.cuda.synchronize()
-    p1_ms, p1_cnt = plan1.read_profile()[dom]
-    plan1.close()
-    one_ms = p1_ms / p1_cnt
-    if dom == "momentum":
-        one_ach = momentum_bytes(wl.shapes, True) / (p1_cnt / one_steps) / (one_ms * 1e-3) / 1e9
-        one_peak = PEAK_HBM_GBS
-    else:
-        one_ach = wl.T * work[dom] / (p1_cnt / one_steps) / (one_ms * 1e-3) / 1e12
-        one_peak = PEAK_BF16_TFLOPS
-    roof_one = {"bound": roof["bound"], "achieved": one_ach, "peak": one_peak, "unit": roof["unit"],
-                "frac": one_ach / one_peak, "kernel": dom, "ms_per_launch": one_ms,
-                "note": f"one-stream plan (groups=1), {one_steps} steps after the timed region"}
 
     out = {
         "metric": "Muon steps/s on GPT-2-small hidden set (T=5); % bf16 MFMA peak",
@@ -285,11 +307,7 @@ def main():
         "kernels": per_kind,
         "kernels_pass": f"{prof_steps} steps after warm-up with every launch timed, outside the timed region",
         "roofline": roof,
-        "roofline_one_stream": roof_one,
-        "schedule": {"coeffs": [list(t) for t in sched], "ms_per_step": sched_ms, "steps_per_s": 1000.0 / sched_ms,
-                     "note": f"muon_step_schedule, {sched_steps} steps after the timed region"},
-        "graph": {"ms_per_step": graph_ms, "steps_per_s": 1000.0 / graph_ms,
-                  "note": f"one step captured in a HIP graph, {graph_steps} replays after the timed region"},
+        **extras,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
