@@ -545,6 +545,36 @@ __device__ __forceinline__ void cblock(const float* ct, int c, int r, float (&bl
   for (int e = 0; e < 4; ++e) crow(ct, c + e, r, blk[e]);
 }
 
+// Row reads of 8 consecutive columns c..c+7 (c a multiple of 8): chunks c/4 and
+// c/4 + 1.  Each of the two LDS reads takes the even chunk on threads with
+// (c / 8) % 16 < 8 and the odd one on the others, so the 16 threads of a row
+// touch 16 distinct bank groups per read (conflict-free under cswz).
+__device__ __forceinline__ void crow8(const float* ct, int r, int c, float* v) {
+  const int odd_first = (c >> 6) & 1;
+  float a[4], b[4];
+  crow(ct, r, c + 4 * odd_first, a);
+  crow(ct, r, c + 4 - 4 * odd_first, b);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[e] = odd_first ? b[e] : a[e];
+    v[4 + e] = odd_first ? a[e] : b[e];
+  }
+}
+__device__ __forceinline__ u32x4 pack8_bf16(const float* v) {
+  const u32x2 a = pack4_bf16(v[0], v[1], v[2], v[3]), b = pack4_bf16(v[4], v[5], v[6], v[7]);
+  return u32x4{a.x, a.y, b.x, b.y};
+}
+__device__ __forceinline__ void unpack8_bf16(u32x4 r, float* v) {
+  unpack4_bf16(u32x2{r.x, r.y}, v);
+  unpack4_bf16(u32x2{r.z, r.w}, v + 4);
+}
+__device__ __forceinline__ u32x4 lo8_bf16(const float* v) {
+  float l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) l[e] = lo_part(v[e]);
+  return pack8_bf16(l);
+}
+
 template <bool F32>
 __device__ __forceinline__ void store4(void* base, size_t off, const float* v) {
   if (F32)
@@ -567,6 +597,34 @@ __device__ __forceinline__ void load4(const void* base, size_t off, float* v) {
     v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
   } else {
     unpack4_bf16(*gv<u32x2>((const uint16_t*)base + off), v);
+  }
+}
+// 8 consecutive elements (16-byte aligned for bf16, 32-byte for fp32)
+template <bool F32>
+__device__ __forceinline__ void store8(void* base, size_t off, const float* v) {
+  if (F32) {
+    store4<true>(base, off, v);
+    store4<true>(base, off + 4, v + 4);
+  } else {
+    *gv<u32x4>((uint16_t*)base + off) = pack8_bf16(v);
+  }
+}
+template <bool F32>
+__device__ __forceinline__ void store8_stream(void* base, size_t off, const float* v) {
+  if (F32) {
+    store4_stream<true>(base, off, v);
+    store4_stream<true>(base, off + 4, v + 4);
+  } else {
+    __builtin_nontemporal_store(pack8_bf16(v), gv<u32x4>((uint16_t*)base + off));
+  }
+}
+template <bool F32>
+__device__ __forceinline__ void load8(const void* base, size_t off, float* v) {
+  if (F32) {
+    load4<true>(base, off, v);
+    load4<true>(base, off + 4, v + 4);
+  } else {
+    unpack8_bf16(*gv<u32x4>((const uint16_t*)base + off), v);
   }
 }
 
@@ -674,6 +732,21 @@ __device__ __forceinline__ void store4_upper(void* out, size_t off, const float*
       }
   }
 }
+template <bool F32>
+__device__ __forceinline__ void store8_upper(void* out, size_t off, const float* v, int r, int c) {
+  if (r <= c) {
+    store8<F32>(out, off, v);
+  } else if (r <= c + 7) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (r <= c + e) {
+        if (F32)
+          gv<float>((float*)out)[off + e] = v[e];
+        else
+          gv<uint16_t>((uint16_t*)out)[off + e] = f2bf(v[e]);
+      }
+  }
+}
 // ... and the strictly lower triangle (row R > column cc + e) from the mirror pass.
 template <bool F32>
 __device__ __forceinline__ void store4_lower(void* out, size_t off, const float* v, int R, int cc) {
@@ -695,34 +768,35 @@ __device__ __forceinline__ void store4_lower(void* out, size_t off, const float*
 // (bf16 products): A at the direct positions (stage 2), X (stage 3: its
 // bf16 copy, plus the low words in the kHiLo variant).  Global stores share the in-order
 // vector-memory counter with loads, so every load of the epilogue is issued
-// before its first store.  Row pass: thread handles tile rows (tid >> 5) + 8 q
-// and columns c..c+3; column pass: the 4x4 block C[c..c+3][r..r+3] with
-// r = 4 (tid >> 5) + 32 q, written as 4 rows of the transposed tile.
+// before its first store.  Row pass: thread handles tile rows (tid >> 4) + 16 q
+// and columns c..c+7 (16-byte bf16 accesses); column pass: the 4x4 block
+// C[c..c+3][r..r+3] with c = 4 (tid & 31), r = 4 (tid >> 5) + 32 q, written
+// as 4 rows of the transposed tile.
 // Stage 3 kernels come in variants: kHiLo (the a*X term reads X as its
 // hi/lo bf16 pair) and kLast (last iteration: the weight step instead of storing X).
 constexpr int kHiLo = 1, kLast = 2;
 
 struct EpiIn {
-  u32x2 dir16[16];  // bf16 at the direct positions (A of stage 2, X of stage 3)
-  u32x2 lo16[16];   // low words of X (stage 3, kHiLo)
+  u32x4 dir[8];  // bf16 at the direct positions (A of stage 2, X of stage 3)
+  u32x4 lo[8];   // low words of X (stage 3, kHiLo)
 };
 
 template <int STAGE, bool F32, int MODE>
 __device__ __forceinline__ void epi_prefetch(const StageArgs& args, const DevMat& d, const TileOps& o, EpiIn& in,
                                              int tid) {
   if (F32) return;  // the fp32 path loads as it goes
-  const int c = 4 * (tid & 31), rbase = tid >> 5;
+  const int c = 8 * (tid & 15), rbase = tid >> 4;
   if (STAGE == 2) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
-      in.dir16[q] = *gv<u32x2>((const uint16_t*)d.a + (size_t)(o.i0 + rbase + 8 * q) * d.mp + o.j0 + c);
+    for (int q = 0; q < 8; ++q)
+      in.dir[q] = *gv<u32x4>((const uint16_t*)d.a + (size_t)(o.i0 + rbase + 16 * q) * d.mp + o.j0 + c);
   } else if (STAGE == 3) {
     const void* xin = xbuf(d, args.t - 1);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const size_t off = (size_t)(o.i0 + rbase + 8 * q) * d.np + o.j0 + c;
-      in.dir16[q] = *gv<u32x2>((const uint16_t*)xin + off);
-      if (MODE & kHiLo) in.lo16[q] = __builtin_nontemporal_load(gv<u32x2>(d.xlo + off));
+    for (int q = 0; q < 8; ++q) {
+      const size_t off = (size_t)(o.i0 + rbase + 16 * q) * d.np + o.j0 + c;
+      in.dir[q] = *gv<u32x4>((const uint16_t*)xin + off);
+      if (MODE & kHiLo) in.lo[q] = __builtin_nontemporal_load(gv<u32x4>(d.xlo + off));
     }
   }
 }
@@ -739,12 +813,13 @@ __device__ __forceinline__ bool epilogue_early(const DevMat& d, const TileOps& o
   if (STAGE == 3) return !((MODE & kLast) && d.transposed);
   return !o.diag;
 }
-// Lower bound of those instructions: the 8 row-pass stores of rows 64..127
-// on the early paths whose store count does not depend on the data.
-template <int STAGE, int MODE>
+// Lower bound of those instructions: the row-pass stores of rows 64..127 (4
+// passes, one 16-byte store each in bf16, two in fp32) on the early paths
+// whose store count does not depend on the data.
+template <int STAGE, bool F32, int MODE>
 __device__ __forceinline__ int epilogue_pending(const DevMat& d, const TileOps& o) {
   if (STAGE == 3 && (MODE & kLast)) return 0;
-  return epilogue_early<STAGE, MODE>(d, o) ? 8 : 0;
+  return epilogue_early<STAGE, MODE>(d, o) ? (F32 ? 8 : 4) : 0;
 }
 
 template <int STAGE, bool F32, int MODE, class NextSlab>
@@ -752,7 +827,8 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
                                               const f32x16 (&acc)[2][2], const EpiIn& in, float* ct, int tid, int lane,
                                               int wm, int wn, NextSlab next_slab) {
   const int t = args.t;
-  const int c = 4 * (tid & 31), rbase = tid >> 5;
+  const int c = 8 * (tid & 15), rbase = tid >> 4;    // row passes
+  const int c4 = 4 * (tid & 31), rb4 = tid >> 5;     // 4x4-block (column) passes
   const int i0 = o.i0, j0 = o.j0;
 
   float pre = 1.f;  // stage 1 of the first iteration works on U: A = s^2 U U^T
@@ -770,8 +846,8 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
   void* xout = xbuf(d, t);
   void* sym_out = STAGE == 1 ? d.a : d.b;
   const bool early = epilogue_early<STAGE, MODE>(d, o);
-  auto hand_over = [&](int q) {  // rows 0..63 are no longer read after row pass 7
-    if (q == 8 && early) {
+  auto hand_over = [&](int q) {  // rows 0..63 are no longer read after row pass 3
+    if (q == 4 && early) {
       MUON_LDS_BARRIER();
       next_slab();
     }
@@ -795,16 +871,16 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
 
   auto in_dir = [&](int q, float* v) {  // epilogue input at the direct position of row pass q
     if (F32) {
-      const size_t off = STAGE == 2 ? (size_t)(i0 + rbase + 8 * q) * d.mp + j0 + c
-                                    : (size_t)(i0 + rbase + 8 * q) * d.np + j0 + c;
-      load4<true>(STAGE == 2 ? (const void*)d.a : xin, off, v);
+      const size_t off = STAGE == 2 ? (size_t)(i0 + rbase + 16 * q) * d.mp + j0 + c
+                                    : (size_t)(i0 + rbase + 16 * q) * d.np + j0 + c;
+      load8<true>(STAGE == 2 ? (const void*)d.a : xin, off, v);
     } else {
-      unpack4_bf16(in.dir16[q], v);
+      unpack8_bf16(in.dir[q], v);
       if (hilo_in) {
-        float l[4];
-        unpack4_bf16(in.lo16[q], l);
+        float l[8];
+        unpack8_bf16(in.lo[q], l);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += l[e];
+        for (int e = 0; e < 8; ++e) v[e] += l[e];
       }
     }
   };
@@ -814,37 +890,37 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
     // itself, a diagonal tile also its strictly lower triangle (below).
     // direct tile (i, j)
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < 8; ++q) {
       hand_over(q);
-      const int r = rbase + 8 * q;
-      float v[4];
-      crow(ct, r, c, v);
+      const int r = rbase + 16 * q;
+      float v[8];
+      crow8(ct, r, c, v);
       if (STAGE == 1) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] *= pre;
+        for (int e = 0; e < 8; ++e) v[e] *= pre;
       } else {
-        float av[4];
+        float av[8];
         in_dir(q, av);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = fmaf(args.c, v[e], args.b * av[e]);
+        for (int e = 0; e < 8; ++e) v[e] = fmaf(args.c, v[e], args.b * av[e]);
       }
       const size_t off = (size_t)(i0 + r) * d.mp + j0 + c;
       if (o.diag)
-        store4_upper<F32>(sym_out, off, v, r, c);
+        store8_upper<F32>(sym_out, off, v, r, c);
       else
-        store4<F32>(sym_out, off, v);
+        store8<F32>(sym_out, off, v);
     }
     // lower triangle of a diagonal tile: row i0 + R, columns i0 + c.. hold C[c..c+3][R]
     if (o.diag) {
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) {
-        const int r = 4 * rbase + 32 * qb;
+        const int r = 4 * rb4 + 32 * qb;
         float blk[4][4];
-        cblock(ct, c, r, blk);
+        cblock(ct, c4, r, blk);
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           float w[4];
-          const size_t off = (size_t)(j0 + r + f) * d.mp + i0 + c;
+          const size_t off = (size_t)(j0 + r + f) * d.mp + i0 + c4;
           if (STAGE == 1) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) w[e] = blk[e][f] * pre;
@@ -854,56 +930,60 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
 #pragma unroll
             for (int e = 0; e < 4; ++e) w[e] = fmaf(args.c, blk[e][f], args.b * av[e]);
           }
-          store4_lower<F32>(sym_out, off, w, r + f, c);
+          store4_lower<F32>(sym_out, off, w, r + f, c4);
         }
       }
     }
   } else {
-    float wrow[16][4];
+    float wrow[8][8];
     if (last && !d.transposed) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) weight_load(d, i0 + rbase + 8 * q, j0 + c, wrow[q]);
+      for (int q = 0; q < 8; ++q) {
+        weight_load(d, i0 + rbase + 16 * q, j0 + c, wrow[q]);
+        weight_load(d, i0 + rbase + 16 * q, j0 + c + 4, wrow[q] + 4);
+      }
     }
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < 8; ++q) {
       hand_over(q);
-      const int r = rbase + 8 * q;
+      const int r = rbase + 16 * q;
       const size_t off = (size_t)(i0 + r) * d.np + j0 + c;
-      float v[4], xv[4];
-      crow(ct, r, c, v);
+      float v[8], xv[8];
+      crow8(ct, r, c, v);
       in_dir(q, xv);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = fmaf(alpha, xv[e], beta * v[e]);
+      for (int e = 0; e < 8; ++e) v[e] = fmaf(alpha, xv[e], beta * v[e]);
       if (!last) {
-        store4_stream<F32>(xout, off, v);
-        if (write_lo)
-          __builtin_nontemporal_store(pack4_bf16(lo_part(v[0]), lo_part(v[1]), lo_part(v[2]), lo_part(v[3])),
-                                      gv<u32x2>(d.xlo + off));
+        store8_stream<F32>(xout, off, v);
+        if (write_lo) __builtin_nontemporal_store(lo8_bf16(v), gv<u32x4>(d.xlo + off));
       } else if (!d.transposed) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = fmaf(-lr_eff, v[e], wrow[q][e]);
+        for (int e = 0; e < 8; ++e) v[e] = fmaf(-lr_eff, v[e], wrow[q][e]);
         weight_store(d, i0 + r, j0 + c, v);
+        weight_store(d, i0 + r, j0 + c + 4, v + 4);
       } else {
-        *(f32x4*)cptr(ct, r, c) = f32x4{v[0], v[1], v[2], v[3]};  // O back into the staged tile
+        // O back into the staged tile
+        *(f32x4*)cptr(ct, r, c) = f32x4{v[0], v[1], v[2], v[3]};
+        *(f32x4*)cptr(ct, r, c + 4) = f32x4{v[4], v[5], v[6], v[7]};
       }
     }
     if (last && d.transposed && j0 < d.n) {
       // W is the transpose of the canonical X: W row (j0 + R) holds O[i0 + c..][j0 + R]
       float wv[16][4];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) weight_load_rows(d, j0 + 4 * rbase + 32 * (q >> 2) + (q & 3), i0 + c, wv[q]);
+      for (int q = 0; q < 16; ++q) weight_load_rows(d, j0 + 4 * rb4 + 32 * (q >> 2) + (q & 3), i0 + c4, wv[q]);
       MUON_LDS_BARRIER();
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) {
-        const int r = 4 * rbase + 32 * qb;
+        const int r = 4 * rb4 + 32 * qb;
         float blk[4][4];
-        cblock(ct, c, r, blk);
+        cblock(ct, c4, r, blk);
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           float w[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) w[e] = fmaf(-lr_eff, blk[e][f], wv[4 * qb + f][e]);
-          weight_store_rows(d, j0 + r + f, i0 + c, w);
+          weight_store_rows(d, j0 + r + f, i0 + c4, w);
         }
       }
     } else if (last && d.transposed) {
@@ -1037,8 +1117,10 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void ns_stage_kernel(StageA
     // the epilogue's inputs.
     auto phase = [&](auto qx, auto px, int kb, int ke) {
       for (int kt = kb; kt < ke; ++kt) {
-        if (kt == 0 && pend >= 8)
+        if (kt == 0 && pend == 8)
           MUON_WAIT_VMCNT(8);  // slab 0 has landed; the last epilogue's final stores may not have
+        else if (kt == 0 && pend == 4)
+          MUON_WAIT_VMCNT(4);
         else
           MUON_WAIT_VMCNT(0);  // this wave's part of slab kt has landed ...
         MUON_LDS_BARRIER();    // ... everyone's, and slab kt - 1 is no longer read
@@ -1092,7 +1174,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void ns_stage_kernel(StageA
       asm volatile("" ::: "memory");  // the epilogue's later memory operations stay after the request
     });
     if (!more) break;
-    pend = epilogue_pending<STAGE, MODE>(d, o);
+    pend = epilogue_pending<STAGE, F32, MODE>(d, o);
     q = qn;
     tl = tn;
     d = load_stage_mat<STAGE, MODE>(args.mats + tl.mat);
