@@ -54,6 +54,23 @@ __device__ __forceinline__ const MUON_GLOBAL V* gv(const T* p) {
 
 // ---------------------------------------------------------------- helpers --
 
+// A plain-typed copy of data the kernel only reads (table entries, a norm
+// scale written by an earlier launch) through the constant address space:
+// uniform addresses then compile to scalar loads, which do not share the
+// in-order vector-memory counter with the epilogue's loads and stores.
+#define MUON_CONST __attribute__((address_space(4)))
+template <class T>
+__device__ __forceinline__ T load_uniform(const T* p) {
+  static_assert(sizeof(T) % 4 == 0, "whole dwords");
+  struct Words {
+    uint32_t w[sizeof(T) / 4];
+  } v;
+  const MUON_CONST uint32_t* s = (const MUON_CONST uint32_t*)(const void*)p;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) v.w[i] = s[i];
+  return __builtin_bit_cast(T, v);
+}
+
 __device__ __forceinline__ uint16_t f2bf(float x) {
   __bf16 h = (__bf16)x;  // v_cvt_pk_bf16_f32: round to nearest even
   return __builtin_bit_cast(uint16_t, h);
@@ -715,55 +732,6 @@ __device__ __forceinline__ bool dma_operand(char* lds, const char* base, uint32_
   return false;
 }
 
-// Writes of the 4 columns c..c+3 of a diagonal tile's row r: only the upper
-// triangle (r <= column) comes from the direct pass.
-template <bool F32>
-__device__ __forceinline__ void store4_upper(void* out, size_t off, const float* v, int r, int c) {
-  if (r <= c) {
-    store4<F32>(out, off, v);
-  } else if (r <= c + 3) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (r <= c + e) {
-        if (F32)
-          gv<float>((float*)out)[off + e] = v[e];
-        else
-          gv<uint16_t>((uint16_t*)out)[off + e] = f2bf(v[e]);
-      }
-  }
-}
-template <bool F32>
-__device__ __forceinline__ void store8_upper(void* out, size_t off, const float* v, int r, int c) {
-  if (r <= c) {
-    store8<F32>(out, off, v);
-  } else if (r <= c + 7) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (r <= c + e) {
-        if (F32)
-          gv<float>((float*)out)[off + e] = v[e];
-        else
-          gv<uint16_t>((uint16_t*)out)[off + e] = f2bf(v[e]);
-      }
-  }
-}
-// ... and the strictly lower triangle (row R > column cc + e) from the mirror pass.
-template <bool F32>
-__device__ __forceinline__ void store4_lower(void* out, size_t off, const float* v, int R, int cc) {
-  if (R > cc + 3) {
-    store4<F32>(out, off, v);
-  } else if (R > cc) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (R > cc + e) {
-        if (F32)
-          gv<float>((float*)out)[off + e] = v[e];
-        else
-          gv<uint16_t>((uint16_t*)out)[off + e] = f2bf(v[e]);
-      }
-  }
-}
-
 // Inputs of a tile's epilogue, prefetched while its last K slab multiplies
 // (bf16 products): A at the direct positions (stage 2), X (stage 3: its
 // bf16 copy, plus the low words in the kHiLo variant).  Global stores share the in-order
@@ -773,8 +741,11 @@ __device__ __forceinline__ void store4_lower(void* out, size_t off, const float*
 // C[c..c+3][r..r+3] with c = 4 (tid & 31), r = 4 (tid >> 5) + 32 q, written
 // as 4 rows of the transposed tile.
 // Stage 3 kernels come in variants: kHiLo (the a*X term reads X as its
-// hi/lo bf16 pair) and kLast (last iteration: the weight step instead of storing X).
-constexpr int kHiLo = 1, kLast = 2;
+// hi/lo bf16 pair), kWriteLo (the new X is written as a hi/lo pair too) and
+// kLast (last iteration: the weight step instead of storing X).  Keeping the
+// epilogue's store count a compile-time constant lets the compiler's waits for
+// the prefetched inputs leave the earlier row passes' stores in flight.
+constexpr int kHiLo = 1, kLast = 2, kWriteLo = 4;
 
 struct EpiIn {
   u32x4 dir[8];  // bf16 at the direct positions (A of stage 2, X of stage 3)
@@ -819,7 +790,7 @@ __device__ __forceinline__ bool epilogue_early(const DevMat& d, const TileOps& o
 template <int STAGE, bool F32, int MODE>
 __device__ __forceinline__ int epilogue_pending(const DevMat& d, const TileOps& o) {
   if (STAGE == 3 && (MODE & kLast)) return 0;
-  return epilogue_early<STAGE, MODE>(d, o) ? (F32 ? 8 : 4) : 0;
+  return epilogue_early<STAGE, MODE>(d, o) ? (F32 || (MODE & kWriteLo) ? 8 : 4) : 0;
 }
 
 template <int STAGE, bool F32, int MODE, class NextSlab>
@@ -832,15 +803,16 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
   const int i0 = o.i0, j0 = o.j0;
 
   float pre = 1.f;  // stage 1 of the first iteration works on U: A = s^2 U U^T
-  if (STAGE == 1 && t == 1) pre = gv<float>(d.sc)[0] * gv<float>(d.sc)[0];
+  // the norm scale through a scalar load: a vector load here would wait for the prefetched inputs
+  if (STAGE == 1 && t == 1) pre = load_uniform(d.sc) * load_uniform(d.sc);
   float alpha = args.a, beta = 1.f;
   if (STAGE == 3 && t == 1) {
-    beta = gv<float>(d.sc)[0];
+    beta = load_uniform(d.sc);
     alpha = args.a * beta;
   }
   constexpr bool last = STAGE == 3 && (MODE & kLast);
   constexpr bool hilo_in = STAGE == 3 && !F32 && (MODE & kHiLo);
-  const bool write_lo = STAGE == 3 && !F32 && !last && t < args.kmaster;
+  constexpr bool write_lo = STAGE == 3 && !F32 && !last && (MODE & kWriteLo);
   const float lr_eff = args.lr * d.scale;
   const void* xin = xbuf(d, t - 1);
   void* xout = xbuf(d, t);
@@ -886,54 +858,44 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
   };
 
   if (STAGE == 1 || STAGE == 2) {
-    // A and B are stored upper-triangle only: an off-diagonal tile writes
-    // itself, a diagonal tile also its strictly lower triangle (below).
-    // direct tile (i, j)
+    // A and B are stored upper-triangle only, except that a diagonal tile is
+    // stored whole: its strictly lower elements are the mirrors C[j][i] of the
+    // upper ones, so both triangles hold exactly the same values.  For stage 2
+    // the input A is read at the direct position in both cases (A's diagonal
+    // tiles are symmetric in memory).  The diagonal case is a separate
+    // instance of the same straight-line pass: every row pass makes one
+    // full-width store, so the compiler's waits are exact in both.
+    auto direct = [&](auto diag_c) {
+      constexpr bool kDiag = decltype(diag_c)::value;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      hand_over(q);
-      const int r = rbase + 16 * q;
-      float v[8];
-      crow8(ct, r, c, v);
-      if (STAGE == 1) {
+      for (int q = 0; q < 8; ++q) {
+        hand_over(q);
+        const int r = rbase + 16 * q;
+        float v[8];
+        crow8(ct, r, c, v);
+        if (kDiag) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] *= pre;
-      } else {
-        float av[8];
-        in_dir(q, av);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = fmaf(args.c, v[e], args.b * av[e]);
-      }
-      const size_t off = (size_t)(i0 + r) * d.mp + j0 + c;
-      if (o.diag)
-        store8_upper<F32>(sym_out, off, v, r, c);
-      else
-        store8<F32>(sym_out, off, v);
-    }
-    // lower triangle of a diagonal tile: row i0 + R, columns i0 + c.. hold C[c..c+3][R]
-    if (o.diag) {
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        const int r = 4 * rb4 + 32 * qb;
-        float blk[4][4];
-        cblock(ct, c4, r, blk);
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          float w[4];
-          const size_t off = (size_t)(j0 + r + f) * d.mp + i0 + c4;
-          if (STAGE == 1) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = blk[e][f] * pre;
-          } else {
-            float av[4];
-            load4<F32>(d.a, off, av);  // A is symmetric: the lower value equals the stored upper one
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = fmaf(args.c, blk[e][f], args.b * av[e]);
+          for (int e = 0; e < 8; ++e) {
+            const float mirror = cptr(ct, c + e, r)[r & 3];  // C[c + e][r]
+            if (c + e < r) v[e] = mirror;
           }
-          store4_lower<F32>(sym_out, off, w, r + f, c4);
         }
+        if (STAGE == 1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] *= pre;
+        } else {
+          float av[8];
+          in_dir(q, av);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = fmaf(args.c, v[e], args.b * av[e]);
+        }
+        store8<F32>(sym_out, (size_t)(i0 + r) * d.mp + j0 + c, v);
       }
-    }
+    };
+    if (o.diag)
+      direct(std::true_type{});
+    else
+      direct(std::false_type{});
   } else {
     float wrow[8][8];
     if (last && !d.transposed) {
@@ -997,21 +959,6 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
 }
 
 
-// A plain-typed copy of a read-only table entry through the constant address
-// space: uniform addresses then compile to scalar loads, which do not share
-// the in-order vector-memory counter with the epilogue's stores.
-#define MUON_CONST __attribute__((address_space(4)))
-template <class T>
-__device__ __forceinline__ T load_uniform(const T* p) {
-  static_assert(sizeof(T) % 4 == 0, "whole dwords");
-  struct Words {
-    uint32_t w[sizeof(T) / 4];
-  } v;
-  const MUON_CONST uint32_t* s = (const MUON_CONST uint32_t*)(const void*)p;
-#pragma unroll
-  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) v.w[i] = s[i];
-  return __builtin_bit_cast(T, v);
-}
 
 // The descriptor fields the product kernels use (the others stay zero):
 // scalar loads of only these keep the persistent loop within the SGPR budget.
@@ -1209,7 +1156,8 @@ hipError_t prepare_stage_kernels() {
   const void* fns[] = {MUON_STAGE_KERNEL(1, false, 0), MUON_STAGE_KERNEL(1, true, 0),
                        MUON_STAGE_KERNEL(2, false, 0), MUON_STAGE_KERNEL(2, true, 0),
                        MUON_STAGE_KERNEL(3, false, 0), MUON_STAGE_KERNEL(3, false, 1),
-                       MUON_STAGE_KERNEL(3, false, 2), MUON_STAGE_KERNEL(3, false, 3),
+                       MUON_STAGE_KERNEL(3, false, 5), MUON_STAGE_KERNEL(3, false, 2),
+                       MUON_STAGE_KERNEL(3, false, 3),
                        MUON_STAGE_KERNEL(3, true, 0),  MUON_STAGE_KERNEL(3, true, 2)};
   for (const void* f : fns) {
     hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kStageLds);
@@ -1221,6 +1169,7 @@ hipError_t prepare_stage_kernels() {
 hipError_t launch_stage(int stage, bool f32, const StageArgs& args, int blocks, hipStream_t stream) {
   const bool last = args.t == args.T;
   const bool hilo = !f32 && args.t <= args.kmaster;
+  const bool write_lo = !f32 && !last && args.t < args.kmaster;
   if (stage == 1) {
     if (f32) { MUON_STAGE_LAUNCH(1, true, 0) }
     MUON_STAGE_LAUNCH(1, false, 0)
@@ -1238,6 +1187,7 @@ hipError_t launch_stage(int stage, bool f32, const StageArgs& args, int blocks, 
       if (hilo) { MUON_STAGE_LAUNCH(3, false, 3) }
       MUON_STAGE_LAUNCH(3, false, 2)
     }
+    if (write_lo) { MUON_STAGE_LAUNCH(3, false, 5) }
     if (hilo) { MUON_STAGE_LAUNCH(3, false, 1) }
     MUON_STAGE_LAUNCH(3, false, 0)
   }
