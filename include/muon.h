@@ -101,8 +101,10 @@ typedef struct muon_options {
   int32_t zero_momentum;  /* != 0: muon_init zeroes every momentum buffer */
   int32_t max_T;          /* largest T muon_step accepts; <= 0 selects 64 */
   int32_t groups;         /* 1: every launch on the caller's stream; 2 (or <= 0,
-                             the default): two matrix groups, each on a stream of
-                             its own (see muon_plan_info.n_groups) */
+                             the default) to 4: that many matrix groups, each on a
+                             stream of its own (see muon_plan_info.n_groups).  Two
+                             measure fastest on MI355X: with 4 hardware queues per
+                             process, more streams start to share queues. */
 } muon_options;
 
 typedef struct muon_plan muon_plan;
@@ -181,8 +183,8 @@ typedef struct muon_plan_info {
   int32_t n_f32_matrices;    /* matrices whose products run in fp32 (see below) */
   int32_t n_groups;          /* matrix groups (contiguous, of equal cost) whose
                                 steps run on streams of their own, forked from
-                                and joined back into the caller's stream (1 or
-                                2): momentum and norm have n_groups launches per
+                                and joined back into the caller's stream (1 to
+                                4): momentum and norm have n_groups launches per
                                 step, a product kind T * n_groups (times the
                                 precisions present) */
 } muon_plan_info;

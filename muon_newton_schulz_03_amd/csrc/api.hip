@@ -50,6 +50,11 @@ constexpr int64_t kMaxDim = 1 << 20;
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
+// The launches of each matrix group (contiguous runs of matrices of about
+// equal Newton-Schulz cost) go to a stream of their own: each group's kernels
+// fill the others' launch gaps and end-of-launch tails.
+constexpr int kGroups = 4;  // at most; options.groups selects how many are used
+
 struct Options {
   int path = MUON_PATH_BF16;
   int kmaster = 3;
@@ -68,7 +73,7 @@ int read_options(const muon_options* o, Options* out) {
     r.zero = o->zero_momentum;
     r.maxT = o->max_T <= 0 ? 64 : o->max_T;
     r.groups = o->groups <= 0 ? 2 : o->groups;
-    if (r.groups > 2) return fail(MUON_E_INVAL, "options.groups %d exceeds 2", r.groups);
+    if (r.groups > kGroups) return fail(MUON_E_INVAL, "options.groups %d exceeds %d", r.groups, kGroups);
     if (r.maxT > 4096) return fail(MUON_E_INVAL, "options.max_T %d exceeds 4096", r.maxT);
     if (r.kmaster > 4096) return fail(MUON_E_INVAL, "options.x_master_iters %d exceeds 4096", r.kmaster);
   }
@@ -108,10 +113,6 @@ int check_desc(const muon_matrix_desc& d, int idx, bool need_ptrs) {
   return MUON_OK;
 }
 
-// The Newton-Schulz launches of the two matrix groups (contiguous halves of
-// equal cost) go to two streams: each group's kernels fill the other's
-// launch gaps and end-of-launch tails.
-constexpr int kGroups = 2;
 
 struct Layout {
   // per matrix byte offsets into the workspace
@@ -188,33 +189,46 @@ std::vector<Tile> xcd_order(const std::vector<std::vector<Tile>>& per_mat, const
   return out;
 }
 
-// Matrices [0, split) form group 0 and [split, n) group 1, split where the
-// running Newton-Schulz cost is closest to half (a single matrix: group 1 is empty).
-int group_split(const std::vector<Geometry>& geo, int groups) {
+// Group g holds matrices [first[g], first[g + 1]): contiguous runs of about
+// equal Newton-Schulz cost, boundary g where the running cost is closest to
+// g / groups of the total (groups beyond the matrix count stay empty).
+void group_bounds(const std::vector<Geometry>& geo, int groups, int (&first)[kGroups + 1]) {
   const int nm = (int)geo.size();
-  if (nm < 2 || groups < 2) return nm;
   std::vector<double> pre(nm + 1, 0.0);
   for (int i = 0; i < nm; ++i) {
     const double m = geo[i].mp, n = geo[i].np;
     pre[i + 1] = pre[i] + m * m * (2.0 * n + m);
   }
-  int best = 1;
-  for (int s = 1; s < nm; ++s)
-    if (std::fabs(2.0 * pre[s] - pre[nm]) < std::fabs(2.0 * pre[best] - pre[nm])) best = s;
-  return best;
+  first[0] = 0;
+  for (int g = 1; g <= kGroups; ++g) {
+    if (g >= groups) {
+      first[g] = nm;
+      continue;
+    }
+    const double target = pre[nm] * g / groups;
+    int best = first[g - 1];
+    for (int s = first[g - 1]; s <= nm; ++s)
+      if (std::fabs(pre[s] - target) < std::fabs(pre[best] - target)) best = s;
+    first[g] = best;
+  }
 }
 
 Tables build_tables(const std::vector<Geometry>& geo, int groups) {
   Tables t;
   const int nm = (int)geo.size();
-  const int split = group_split(geo, groups);
+  group_bounds(geo, groups, t.first);
+  auto group_of = [&](int i) {
+    int g = 0;
+    while (i >= t.first[g + 1]) ++g;
+    return g;
+  };
   for (int grp = 0; grp < kGroups; ++grp)
   for (int prec = 0; prec < 2; ++prec) {
     std::vector<std::vector<Tile>> sym(nm), upd(nm);
     std::vector<double> gram_cost(nm), poly_cost(nm), upd_cost(nm);
     for (int i = 0; i < nm; ++i) {
       const Geometry& g = geo[i];
-      if (g.f32 != prec || (i < split) != (grp == 0)) continue;
+      if (g.f32 != prec || group_of(i) != grp) continue;
       const int tm = g.mp / kTile, tn = g.np / kTile;
       for (int a = 0; a < tm; ++a)
         for (int b = a; b < tm; ++b) sym[i].push_back(Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0});
@@ -232,13 +246,10 @@ Tables build_tables(const std::vector<Geometry>& geo, int groups) {
   }
   for (int i = 0; i < nm; ++i) {
     const Geometry& g = geo[i];
-    std::vector<Tile>& mom = t.mom[i < split ? 0 : 1];
+    std::vector<Tile>& mom = t.mom[group_of(i)];
     for (int a = 0; a < g.mp / kMomTile; ++a)
       for (int b = 0; b < g.np / kMomTile; ++b) mom.push_back(Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0});
   }
-  t.first[0] = 0;
-  t.first[1] = split;
-  t.first[2] = nm;
   return t;
 }
 

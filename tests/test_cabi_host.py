@@ -140,10 +140,16 @@ def test_groups_option():
     d1, t1 = describe(g.shapes, kind=_lib.KIND_UPDATE, groups=1)
     d2, t2 = describe(g.shapes, kind=_lib.KIND_UPDATE)
     assert sorted(t for t in t1 if t[0] >= 0) == sorted(t for t in t2 if t[0] >= 0)
+    # up to 4 groups; more matrices than groups fill all of them, fewer leave some empty
+    for ng in (3, 4):
+        d, t = describe(g.shapes, kind=_lib.KIND_UPDATE, groups=ng)
+        assert d["n_groups"] == ng
+        assert sorted(x for x in t if x[0] >= 0) == sorted(x for x in t1 if x[0] >= 0)
+    assert describe([(768, 768), (768, 3072)], groups=4)[0]["n_groups"] == 2
     lib = _lib.load()
     arr = descs([(64, 64)])
     info = _lib.PlanInfo()
-    rc = lib.muon_describe(arr, 1, ctypes.byref(Options(0, -1, 0, 0, 3)), ctypes.byref(info), -1, None, 0, None)
+    rc = lib.muon_describe(arr, 1, ctypes.byref(Options(0, -1, 0, 0, 5)), ctypes.byref(info), -1, None, 0, None)
     assert rc == _lib.MUON_E_INVAL and "groups" in _lib.last_error()
 
 
