@@ -51,10 +51,10 @@ def momentum_bytes(shapes, master: bool):
     return p * (2 + 4 + 4 + 2 + (2 if master else 0))
 
 
-def read_traffic(kind: str):
-    """HBM bytes per launch of one kernel kind from the committed rocprofv3 counter
-    summary; None when there is none or the kernels changed since it was taken."""
-    path = os.path.join(PROFILES, f"{WORKLOAD}_hbm_traffic.txt")
+def read_profile_value(summary: str, key: str):
+    """One value of a committed rocprofv3 counter summary (profiles/); None when
+    there is none or the kernels changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{WORKLOAD}_{summary}.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -66,9 +66,14 @@ def read_traffic(kind: str):
     if vals.get("kernel_source_hash") != kernel_source_hash():
         return None
     try:
-        return float(vals[f"{kind}_hbm_bytes_per_launch"])
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
+
+
+def read_traffic(kind: str):
+    """HBM bytes per launch of one kernel kind (FETCH_SIZE + WRITE_SIZE, calibrated)."""
+    return read_profile_value("hbm_traffic", f"{kind}_hbm_bytes_per_launch")
 
 
 def cpu_baseline(wl, budget_s: float = 12.0):
@@ -190,6 +195,8 @@ def main():
     ap.add_argument("--x-master-iters", type=int, default=-1)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 256 MiB device copy first (counter calibration)")
+    ap.add_argument("--calibrate-mfma", action="store_true",
+                    help="run a bf16 8192^3 torch GEMM three times first (MFMA-counter reference)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the Muon step here has no multi-GPU path "
@@ -215,6 +222,15 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.calibrate_mfma:
+        # a library GEMM of known FLOPs: its MFMA-busy reading and its FLOP rate
+        # at its own clock check the counter normalisation (outside the Muon path)
+        ga = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+        gb = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+        for _ in range(3):
+            gc = ga @ gb
+        torch.cuda.synchronize()
+        del ga, gb, gc
     plan = MuonStep(W, grads[0], M, x_master_iters=args.x_master_iters)
     kw = dict(a=wl.coeffs[0], b=wl.coeffs[1], c=wl.coeffs[2], T=wl.T, momentum=wl.momentum,
               nesterov=wl.nesterov, lr=wl.lr)
@@ -281,6 +297,8 @@ def main():
     roof["ms_per_launch"] = d_launch_ms
     roof["launches_per_step"] = d_cnt / args.steps
     roof["traffic"] = read_traffic(dom)
+    # share of SIMD cycles with the MFMA unit busy (rocprofv3 counters), when fresh
+    roof["mfma_busy"] = read_profile_value("mfma_busy", f"{dom}_mfma_busy")
     roof["note"] = ("the plan runs two matrix groups on two streams, so each launch covers half the set "
                     "and shares the GPU with the other group's launches")
 

@@ -7,10 +7,18 @@ Two summaries:
   average durations, plus the per-dispatch durations of the product kernels;
 * HBM traffic from two ``--pmc`` runs (``FETCH_SIZE``, then ``WRITE_SIZE``,
   KiB per dispatch) of ``bench.py --calibrate-copy``, scaled by what the same
-  counters read for the plain copy kernel of known size that run contains.
+  counters read for the plain copy kernel of known size that run contains;
+* MFMA busy from one ``--pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE`` run of
+  ``bench.py --calibrate-mfma``: busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs
+  x GRBM_GUI_ACTIVE / 8 XCDs), i.e. the share of SIMD cycles whose MFMA unit
+  is busy (the first counter sums over all SIMDs, the second over the XCDs).
+  The run's library GEMM (bf16 8192^3) checks both sums: its busy cycles x
+  1024 FLOP must equal its known FLOPs, and the clock GRBM_GUI_ACTIVE / 8 /
+  dispatch time must stay within the chip's 2.4 GHz.
 
     python -m muon_newton_schulz_03_amd.rocprof_summary stats  <trace_dir> <out.txt> "<command>"
     python -m muon_newton_schulz_03_amd.rocprof_summary traffic <fetch_dir> <write_dir> <out.txt> "<commands>"
+    python -m muon_newton_schulz_03_amd.rocprof_summary mfma    <pmc_dir> <out.txt> "<command>"
 """
 from __future__ import annotations
 
@@ -135,6 +143,54 @@ def traffic_summary(fetch_dir: str, write_dir: str, command: str) -> str:
     return "\n".join(out) + "\n"
 
 
+N_XCD = 8          # MI355X: XCDs (GRBM_GUI_ACTIVE sums over them)
+N_SIMD = 256 * 4   # MI355X: CUs x SIMDs (SQ_VALU_MFMA_BUSY_CYCLES sums over them)
+GEMM_FLOPS = 2.0 * 8192 ** 3
+PEAK_BF16_PER_CLOCK = 256 * 4096.0  # dense bf16 FLOP per clock (2.5 PFLOP/s at 2.4 GHz)
+
+
+def mfma_summary(pmc_dir: str, command: str) -> str:
+    rows = list(csv.DictReader(open(_one(os.path.join(pmc_dir, "**", "*counter_collection.csv")))))
+    disp = defaultdict(dict)
+    for r in rows:
+        d = disp[r["Dispatch_Id"]]
+        d["name"] = r["Kernel_Name"]
+        d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    per_kind = defaultdict(list)
+    gemm = []
+    for d in disp.values():
+        if "SQ_VALU_MFMA_BUSY_CYCLES" not in d or "GRBM_GUI_ACTIVE" not in d or d["GRBM_GUI_ACTIVE"] <= 0:
+            continue
+        busy = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * d["GRBM_GUI_ACTIVE"] / N_XCD)
+        clock = d["GRBM_GUI_ACTIVE"] / N_XCD / d["ns"]  # GHz
+        k = kind_of(d["name"])
+        if k:
+            per_kind[k].append((busy, clock))
+        elif busy > 0.2 and d["ns"] > 200_000:  # the calibration GEMM (the only other MFMA kernel)
+            # one busy SIMD cycle of a bf16 32x32x16 / 16x16x32 MFMA is 1024 FLOP
+            gemm.append((busy, clock, d["SQ_VALU_MFMA_BUSY_CYCLES"] * 1024.0 / GEMM_FLOPS))
+    out = ["# MFMA busy per dispatch from rocprofv3 counters (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE)",
+           f"# command: {command}",
+           f"# busy = SQ_VALU_MFMA_BUSY_CYCLES / ({N_SIMD} SIMDs x GRBM_GUI_ACTIVE / {N_XCD} XCDs), mean over"
+           " dispatches; the timer window of a short dispatch includes a few idle microseconds, so short"
+           " kernels read slightly low",
+           f"kernel_source_hash = {kernel_source_hash()}"]
+    for k in ("momentum", "gram", "poly", "update"):
+        v = per_kind.get(k)
+        if not v:
+            continue
+        out.append(f"{k}_mfma_busy = {sum(b for b, _ in v) / len(v):.4f}")
+    if gemm:
+        out.append("# reference: library bf16 GEMM 8192^3.  Its busy SIMD cycles x 1024 FLOP should equal its")
+        out.append("# 2 * 8192^3 FLOP (ratio 1: the counter sums over SIMDs), and the clock GRBM_GUI_ACTIVE / 8 /")
+        out.append("# dispatch time of this long dispatch should stay within the 2.4 GHz maximum (the timer sums over XCDs).")
+        out.append(f"gemm_mfma_busy = {sum(g[0] for g in gemm) / len(gemm):.4f}")
+        out.append(f"gemm_clock_ghz = {sum(g[1] for g in gemm) / len(gemm):.3f}")
+        out.append(f"gemm_counted_over_known_flops = {sum(g[2] for g in gemm) / len(gemm):.4f}")
+    return "\n".join(out) + "\n"
+
+
 def main(argv):
     if argv[0] == "stats":
         text = stats_summary(argv[1], argv[3])
@@ -142,6 +198,9 @@ def main(argv):
     elif argv[0] == "traffic":
         text = traffic_summary(argv[1], argv[2], argv[4])
         out = argv[3]
+    elif argv[0] == "mfma":
+        text = mfma_summary(argv[1], argv[3])
+        out = argv[2]
     else:
         raise SystemExit(__doc__)
     with open(out, "w") as f:
