@@ -155,36 +155,67 @@ struct Tables {
   int first[kGroups + 1] = {};          // group g holds matrices first[g] .. first[g+1]-1
 };
 
+// Product launches run kXcds * kBlocksPerXcd blocks (two resident blocks on
+// each of the 32 CUs of an XCD), and block b takes table entries b, b + 512,
+// b + 1024, ...  The tables are laid out for that stride.
+constexpr int kBlocksPerXcd = 64;
+constexpr int kProductGrid = kXcds * kBlocksPerXcd;
+
 // Tiles of one kind, ordered for the MI355X dispatcher, which places block b
-// on XCD b % 8.  All tiles are listed matrix by matrix (most expensive
-// matrices first), the list is cut into 8 contiguous runs of equal total cost,
-// and run x is laid on blocks x, x+8, x+16, ...  Each XCD therefore works on
-// few matrices at a time (they stay in its L2) and the XCDs get equal work;
-// shorter runs are padded with null tiles that exit at once.
+// on XCD b % 8.  The tiles of each cost class are listed matrix by matrix and
+// cut into 8 contiguous runs of equal total cost; XCD x gets run x of every
+// class, most expensive class first.  Each XCD therefore works on few
+// matrices at a time (they stay in its L2) and the XCDs get equal work.
+// Inside a run, each tile in turn goes to the block with the least work so far
+// (longest tiles first, ties to the lowest block), the schedule the blocks
+// would reach if each took the next tile when it finished.  Block j of XCD x
+// (block index 8j + x) finds its r-th tile at entry 8(r * kBlocksPerXcd + j) + x;
+// entries of blocks with fewer tiles hold null tiles that exit at once.
 std::vector<Tile> xcd_order(const std::vector<std::vector<Tile>>& per_mat, const std::vector<double>& tile_cost) {
   const int nm = (int)per_mat.size();
   std::vector<int> order(nm);
   for (int i = 0; i < nm; ++i) order[i] = i;
   std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return tile_cost[x] > tile_cost[y]; });
-  double total = 0.0;
-  for (int i = 0; i < nm; ++i) total += tile_cost[i] * per_mat[i].size();
-  if (total <= 0.0) return {};
   std::vector<std::vector<Tile>> runs(kXcds);
-  double acc = 0.0;
-  for (int i : order) {
-    for (const Tile& t : per_mat[i]) {
-      // the run whose cost share contains the midpoint of this tile
-      int x = (int)((acc + 0.5 * tile_cost[i]) * kXcds / total);
-      x = std::min(std::max(x, 0), kXcds - 1);
-      runs[x].push_back(t);
-      acc += tile_cost[i];
+  // one cost class (matrices whose tiles cost the same) at a time, so that
+  // every XCD gets its share of long and of short tiles
+  for (size_t c0 = 0; c0 < order.size();) {
+    size_t c1 = c0;
+    double total = 0.0;
+    while (c1 < order.size() && tile_cost[order[c1]] == tile_cost[order[c0]])
+      total += tile_cost[order[c1]] * per_mat[order[c1]].size(), ++c1;
+    double acc = 0.0;
+    for (size_t q = c0; q < c1 && total > 0.0; ++q) {
+      const int i = order[q];
+      for (const Tile& t : per_mat[i]) {
+        // the run whose cost share contains the midpoint of this tile
+        int x = (int)((acc + 0.5 * tile_cost[i]) * kXcds / total);
+        x = std::min(std::max(x, 0), kXcds - 1);
+        runs[x].push_back(t);
+        acc += tile_cost[i];
+      }
+    }
+    c0 = c1;
+  }
+  // per XCD: the tiles of each block, in the order the block runs them
+  std::vector<std::vector<Tile>> blk((size_t)kXcds * kBlocksPerXcd);
+  size_t rounds = 0;
+  for (int x = 0; x < kXcds; ++x) {
+    std::vector<double> load(kBlocksPerXcd, 0.0);
+    for (const Tile& t : runs[x]) {
+      const int j = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+      load[j] += tile_cost[t.mat];
+      std::vector<Tile>& l = blk[(size_t)x * kBlocksPerXcd + j];
+      l.push_back(t);
+      rounds = std::max(rounds, l.size());
     }
   }
-  size_t longest = 0;
-  for (int x = 0; x < kXcds; ++x) longest = std::max(longest, runs[x].size());
-  std::vector<Tile> out(longest * kXcds, Tile{kNullMat, 0, 0, 0});
+  std::vector<Tile> out(rounds * kProductGrid, Tile{kNullMat, 0, 0, 0});
   for (int x = 0; x < kXcds; ++x)
-    for (size_t q = 0; q < runs[x].size(); ++q) out[q * kXcds + x] = runs[x][q];
+    for (int j = 0; j < kBlocksPerXcd; ++j) {
+      const std::vector<Tile>& l = blk[(size_t)x * kBlocksPerXcd + j];
+      for (size_t r = 0; r < l.size(); ++r) out[(r * kBlocksPerXcd + j) * kXcds + x] = l[r];
+    }
   while (!out.empty() && out.back().mat == kNullMat) out.pop_back();
   return out;
 }
@@ -319,7 +350,6 @@ struct muon_plan {
   char* ws = nullptr;
   size_t ws_bytes = 0;
   std::vector<DevMat> hmat;            // host image of the current table
-  int cus = 256;                       // compute units of the device (persistent grids)
   DevMat* host_slots[kSlots] = {};     // pinned staging, one per device slot
   hipEvent_t slot_ev[kSlots] = {};
   bool slot_used[kSlots] = {};
@@ -582,13 +612,6 @@ int muon_init(const muon_matrix_desc* descs, int n, const muon_options* opts, vo
   }
   e = prepare_stage_kernels();
   if (e != hipSuccess) return cleanup(hip_fail(e, "hipFuncSetAttribute(dynamic LDS)"));
-  {
-    int dev = 0, cus = 0;
-    e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return cleanup(hip_fail(e, "hipDeviceGetAttribute(CU count)"));
-    if (cus > 0) p->cus = cus;
-  }
 
   // Tile tables: staged through pinned memory, uploaded once; init waits for
   // them so the staging can be released.
@@ -731,10 +754,9 @@ static int step_impl(muon_plan* p, const muon_matrix_desc* descs, int n, const f
           const float* tc = sched ? sched + 3 * (t - 1) : nullptr;
           StageArgs sa{mats, (const Tile*)(p->ws + p->lay.ns_tiles[grp][prec][k]), ntab, t, T, p->opt.kmaster,
                        tc ? tc[0] : a, tc ? tc[1] : b, tc ? tc[2] : c, lr};
-          // persistent grid: two blocks per CU, a multiple of 8 (every block
-          // keeps the XCD of the table entries it takes), never more than the table
-          const int slots = std::max(8, (2 * p->cus) / 8 * 8);
-          const int grid = std::min((ntab + 7) / 8 * 8, slots);
+          // the stride the table was laid out for, or fewer blocks when the
+          // table is shorter (a multiple of 8: every block keeps its XCD)
+          const int grid = std::min((ntab + 7) / 8 * 8, kProductGrid);
           if ((rc = prof_begin(p, kKinds[k], s, &pi))) return rc;
           if ((rc = check_launch(launch_stage(k + 1, prec == 1, sa, grid, s), kNames[k]))) return rc;
           if ((rc = prof_end(p, s, pi))) return rc;

@@ -95,6 +95,33 @@ def test_tile_lists_cover_each_tile_once(shapes):
         assert info["blocks"][kind] == len(tiles)
 
 
+def test_block_loads_are_balanced():
+    # Product launches run 512 blocks; block b takes entries b, b + 512, ...
+    # Inside each XCD each tile in turn (longest first) goes to the least-loaded
+    # block, so the loads of an XCD's blocks differ by at most one tile.
+    g = inputs.workload("gpt2_small")
+    grid = 512
+    for kind in (_lib.KIND_GRAM, _lib.KIND_POLY, _lib.KIND_UPDATE):
+        _, tiles = describe(g.shapes, kind=kind, groups=1)
+        load = Counter()
+        biggest = 0
+        for e, (mat, _, _) in enumerate(tiles):
+            if mat < 0:
+                continue
+            r, c = g.shapes[mat]
+            cost = max(r, c) if kind == _lib.KIND_GRAM else min(r, c)
+            load[e % grid] += cost
+            biggest = max(biggest, cost)
+        for x in range(8):
+            per_block = [load[b] for b in range(x, grid, 8)]
+            assert max(per_block) - min(per_block) <= biggest
+        # every XCD holds the long (K = 3072) Gram tiles as well as the short ones
+        if kind == _lib.KIND_GRAM:
+            for x in range(8):
+                costs = {max(g.shapes[m]) for e, (m, _, _) in enumerate(tiles) if m >= 0 and e % 8 == x}
+                assert costs == {768, 3072}
+
+
 def test_xcd_runs_are_balanced():
     g = inputs.workload("gpt2_small")
     for kind in (_lib.KIND_GRAM, _lib.KIND_POLY, _lib.KIND_UPDATE):
