@@ -309,7 +309,7 @@ size_t layout(const std::vector<Geometry>& geo, const Options& o, const Tables& 
     m.xlo = (size_t)-1;
     if (!g.f32 && o.kmaster > 0) {
       m.xlo = off;
-      off = align_up(off + xe * 2, kAlign);
+      off = align_up(off + xe, kAlign);  // one low byte per element
     }
     m.xo0 = off;
     off = align_up(off + xe * es, kAlign);
@@ -379,7 +379,7 @@ DevMat make_devmat(const muon_plan* p, int i) {
   r.w = d.weight;
   r.g = d.grad;
   r.mom = d.momentum;
-  r.xlo = m.xlo == (size_t)-1 ? nullptr : (uint16_t*)(p->ws + m.xlo);
+  r.xlo = m.xlo == (size_t)-1 ? nullptr : (uint8_t*)(p->ws + m.xlo);
   r.xo[0] = p->ws + m.xo0;
   r.xo[1] = p->ws + m.xo1;
   r.a = p->ws + m.a;
@@ -726,45 +726,56 @@ static int step_impl(muon_plan* p, const muon_matrix_desc* descs, int n, const f
       if (busy[grp]) e = hipStreamWaitEvent(p->gs[grp], p->fork_ev, 0);
     if (e != hipSuccess) return hip_fail(e, "fork of the group streams");
   }
-  for (int grp = 0; grp < kGroups; ++grp) {
-    if (!busy[grp]) continue;
+  // Launch phase 0 is momentum plus norm (or apply when T = 0); phase
+  // 3 (t - 1) + k + 1 is product k of iteration t.  The groups' launches are
+  // enqueued phase by phase, alternating between the groups, so that every
+  // group stream has work queued early even when the host enqueues slower
+  // than the GPU runs.
+  auto enqueue = [&](int grp, int phase) -> int {
     hipStream_t s = fork ? p->gs[grp] : stream;
-    const Tile* mom_tiles = (const Tile*)(p->ws + p->lay.mom_tiles[grp]);
-    const int nmom = (int)p->tab.mom[grp].size();
-    MomArgs ma{mats, mom_tiles, momentum, nesterov ? 1 : 0};
-    if ((rc = prof_begin(p, MUON_KIND_MOMENTUM, s, &pi))) return rc;
-    if ((rc = check_launch(launch_momentum(ma, nmom, s), "momentum launch"))) return rc;
-    if ((rc = prof_end(p, s, pi))) return rc;
-    if (T == 0) {
-      ApplyArgs aa{mats, mom_tiles, lr};
-      if ((rc = prof_begin(p, MUON_KIND_APPLY, s, &pi))) return rc;
-      if ((rc = check_launch(launch_apply(aa, nmom, s), "apply launch"))) return rc;
+    if (phase == 0) {
+      const Tile* mom_tiles = (const Tile*)(p->ws + p->lay.mom_tiles[grp]);
+      const int nmom = (int)p->tab.mom[grp].size();
+      MomArgs ma{mats, mom_tiles, momentum, nesterov ? 1 : 0};
+      if ((rc = prof_begin(p, MUON_KIND_MOMENTUM, s, &pi))) return rc;
+      if ((rc = check_launch(launch_momentum(ma, nmom, s), "momentum launch"))) return rc;
       if ((rc = prof_end(p, s, pi))) return rc;
-    } else {
-      const int f0 = p->tab.first[grp], nf = p->tab.first[grp + 1] - f0;
-      if ((rc = prof_begin(p, MUON_KIND_NORM, s, &pi))) return rc;
-      if ((rc = check_launch(launch_norm(mats + f0, nf, s), "norm launch"))) return rc;
-      if ((rc = prof_end(p, s, pi))) return rc;
-    }
-    for (int t = 1; t <= T; ++t) {
-      for (int k = 0; k < 3; ++k) {
-        for (int prec = 0; prec < 2; ++prec) {
-          const int ntab = (int)p->tab.ns[grp][prec][k].size();
-          if (!ntab) continue;
-          const float* tc = sched ? sched + 3 * (t - 1) : nullptr;
-          StageArgs sa{mats, (const Tile*)(p->ws + p->lay.ns_tiles[grp][prec][k]), ntab, t, T, p->opt.kmaster,
-                       tc ? tc[0] : a, tc ? tc[1] : b, tc ? tc[2] : c, lr};
-          // the stride the table was laid out for, or fewer blocks when the
-          // table is shorter (a multiple of 8: every block keeps its XCD)
-          const int grid = std::min((ntab + 7) / 8 * 8, kProductGrid);
-          if ((rc = prof_begin(p, kKinds[k], s, &pi))) return rc;
-          if ((rc = check_launch(launch_stage(k + 1, prec == 1, sa, grid, s), kNames[k]))) return rc;
-          if ((rc = prof_end(p, s, pi))) return rc;
-        }
+      if (T == 0) {
+        ApplyArgs aa{mats, mom_tiles, lr};
+        if ((rc = prof_begin(p, MUON_KIND_APPLY, s, &pi))) return rc;
+        if ((rc = check_launch(launch_apply(aa, nmom, s), "apply launch"))) return rc;
+        if ((rc = prof_end(p, s, pi))) return rc;
+      } else {
+        const int f0 = p->tab.first[grp], nf = p->tab.first[grp + 1] - f0;
+        if ((rc = prof_begin(p, MUON_KIND_NORM, s, &pi))) return rc;
+        if ((rc = check_launch(launch_norm(mats + f0, nf, s), "norm launch"))) return rc;
+        if ((rc = prof_end(p, s, pi))) return rc;
       }
+      return MUON_OK;
     }
-    if (fork) {
-      e = hipEventRecord(p->join_ev[grp], s);
+    const int t = (phase - 1) / 3 + 1, k = (phase - 1) % 3;
+    for (int prec = 0; prec < 2; ++prec) {
+      const int ntab = (int)p->tab.ns[grp][prec][k].size();
+      if (!ntab) continue;
+      const float* tc = sched ? sched + 3 * (t - 1) : nullptr;
+      StageArgs sa{mats, (const Tile*)(p->ws + p->lay.ns_tiles[grp][prec][k]), ntab, t, T, p->opt.kmaster,
+                   tc ? tc[0] : a, tc ? tc[1] : b, tc ? tc[2] : c, lr};
+      // the stride the table was laid out for, or fewer blocks when the
+      // table is shorter (a multiple of 8: every block keeps its XCD)
+      const int grid = std::min((ntab + 7) / 8 * 8, kProductGrid);
+      if ((rc = prof_begin(p, kKinds[k], s, &pi))) return rc;
+      if ((rc = check_launch(launch_stage(k + 1, prec == 1, sa, grid, s), kNames[k]))) return rc;
+      if ((rc = prof_end(p, s, pi))) return rc;
+    }
+    return MUON_OK;
+  };
+  for (int phase = 0; phase <= 3 * T; ++phase)
+    for (int grp = 0; grp < kGroups; ++grp)
+      if (busy[grp] && (rc = enqueue(grp, phase))) return rc;
+  if (fork) {
+    for (int grp = 0; grp < kGroups; ++grp) {
+      if (!busy[grp]) continue;
+      e = hipEventRecord(p->join_ev[grp], p->gs[grp]);
       if (e == hipSuccess) e = hipStreamWaitEvent(stream, p->join_ev[grp], 0);
       if (e != hipSuccess) return hip_fail(e, "join of the group streams");
     }

@@ -76,10 +76,24 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
   return __builtin_bit_cast(uint16_t, h);
 }
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-// Low word of the hi/lo bf16 pair that carries X in more precision than one
-// bf16: hi = bf16(x) is the operand copy itself, lo = bf16(x - hi) (x - hi is
-// exact in fp32), and hi + lo holds about 16 significant bits of x.
-__device__ __forceinline__ float lo_part(float x) { return x - bf2f(f2bf(x)); }
+// Low byte of the (hi, lo) pair that carries X in more precision than one
+// bf16.  hi = bf16(x) is the operand copy itself; lo is x - hi (exact in
+// fp32, at most half a unit in the last place of hi) as a signed count of
+// 1/256 of that unit, rounded to nearest and held in [-127, 127].  hi + lo
+// then holds about 16 significant bits of x.  The unit is 2^(E - 134) for hi's
+// biased exponent E, so lo counts 2^(max(E, 16) - 142); the floor at E = 16
+// (|hi| < 2^-111) keeps both scale factors normal floats.
+__device__ __forceinline__ int lo_exp(uint16_t hi) { return max((int)((hi >> 7) & 0xFF), 16); }
+__device__ __forceinline__ uint32_t lo_byte(float x) {
+  const uint16_t hi = f2bf(x);
+  const float inv = __uint_as_float((uint32_t)(269 - lo_exp(hi)) << 23);  // 2^(142 - E)
+  const float q = rintf(fminf(fmaxf((x - bf2f(hi)) * inv, -127.f), 127.f));
+  return (uint32_t)(int)q & 0xFFu;
+}
+__device__ __forceinline__ float lo_value(uint16_t hi, uint32_t byte) {
+  const float unit = __uint_as_float((uint32_t)(lo_exp(hi) - 15) << 23);  // 2^(E - 142)
+  return (float)(int)(int8_t)byte * unit;
+}
 
 __device__ __forceinline__ u32x2 pack4_bf16(float a, float b, float c, float d) {
   u32x2 r;
@@ -92,6 +106,17 @@ __device__ __forceinline__ void unpack4_bf16(u32x2 r, float* v) {
   v[1] = __uint_as_float(r.x & 0xFFFF0000u);
   v[2] = __uint_as_float(r.y << 16);
   v[3] = __uint_as_float(r.y & 0xFFFF0000u);
+}
+// Low bytes of 4 values, packed little-endian into one word.
+__device__ __forceinline__ uint32_t pack4_lo(const float* v) {
+  return lo_byte(v[0]) | (lo_byte(v[1]) << 8) | (lo_byte(v[2]) << 16) | (lo_byte(v[3]) << 24);
+}
+// v[e] += the low part of element e, given the 4 bf16 hi words (packed as by
+// pack4_bf16) and their 4 low bytes.
+__device__ __forceinline__ void add4_lo(u32x2 hi, uint32_t lo, float* v) {
+  const uint16_t h[4] = {(uint16_t)hi.x, (uint16_t)(hi.x >> 16), (uint16_t)hi.y, (uint16_t)(hi.y >> 16)};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] += lo_value(h[e], (lo >> (8 * e)) & 0xFFu);
 }
 
 // LDS row swizzle: 16-byte chunk c of tile row r lives at chunk c ^ swz(r).
@@ -240,11 +265,7 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(MomArgs args) {
       const u32x2 h0 = pack4_bf16(xv[q][0], xv[q][1], xv[q][2], xv[q][3]);
       const u32x2 h1 = pack4_bf16(xv[q][4], xv[q][5], xv[q][6], xv[q][7]);
       *gv<u32x4>((uint16_t*)d.xo[0] + xo) = u32x4{h0.x, h0.y, h1.x, h1.y};
-      if (d.xlo) {
-        const u32x2 l0 = pack4_bf16(lo_part(xv[q][0]), lo_part(xv[q][1]), lo_part(xv[q][2]), lo_part(xv[q][3]));
-        const u32x2 l1 = pack4_bf16(lo_part(xv[q][4]), lo_part(xv[q][5]), lo_part(xv[q][6]), lo_part(xv[q][7]));
-        *gv<u32x4>(d.xlo + xo) = u32x4{l0.x, l0.y, l1.x, l1.y};
-      }
+      if (d.xlo) *gv<u32x2>(d.xlo + xo) = u32x2{pack4_lo(xv[q]), pack4_lo(xv[q] + 4)};
     }
   }
 
@@ -354,13 +375,9 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs args) {
       f32x4 v = *gv<f32x4>((const float*)d.xo[0] + xo);
       u[0] = v.x; u[1] = v.y; u[2] = v.z; u[3] = v.w;
     } else {
-      unpack4_bf16(*gv<u32x2>((const uint16_t*)d.xo[0] + xo), u);
-      if (d.xlo) {
-        float l[4];
-        unpack4_bf16(*gv<u32x2>(d.xlo + xo), l);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) u[e] += l[e];
-      }
+      const u32x2 hi = *gv<u32x2>((const uint16_t*)d.xo[0] + xo);
+      unpack4_bf16(hi, u);
+      if (d.xlo) add4_lo(hi, *gv<uint32_t>(d.xlo + xo), u);
     }
     weight_step(d, i, j, u, lr_eff);
   }
@@ -585,12 +602,7 @@ __device__ __forceinline__ void unpack8_bf16(u32x4 r, float* v) {
   unpack4_bf16(u32x2{r.x, r.y}, v);
   unpack4_bf16(u32x2{r.z, r.w}, v + 4);
 }
-__device__ __forceinline__ u32x4 lo8_bf16(const float* v) {
-  float l[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) l[e] = lo_part(v[e]);
-  return pack8_bf16(l);
-}
+__device__ __forceinline__ u32x2 lo8(const float* v) { return u32x2{pack4_lo(v), pack4_lo(v + 4)}; }
 
 template <bool F32>
 __device__ __forceinline__ void store4(void* base, size_t off, const float* v) {
@@ -749,7 +761,7 @@ constexpr int kHiLo = 1, kLast = 2, kWriteLo = 4;
 
 struct EpiIn {
   u32x4 dir[8];  // bf16 at the direct positions (A of stage 2, X of stage 3)
-  u32x4 lo[8];   // low words of X (stage 3, kHiLo)
+  u32x2 lo[8];   // low bytes of X (stage 3, kHiLo)
 };
 
 template <int STAGE, bool F32, int MODE>
@@ -767,7 +779,7 @@ __device__ __forceinline__ void epi_prefetch(const StageArgs& args, const DevMat
     for (int q = 0; q < 8; ++q) {
       const size_t off = (size_t)(o.i0 + rbase + 16 * q) * d.np + o.j0 + c;
       in.dir[q] = *gv<u32x4>((const uint16_t*)xin + off);
-      if (MODE & kHiLo) in.lo[q] = __builtin_nontemporal_load(gv<u32x4>(d.xlo + off));
+      if (MODE & kHiLo) in.lo[q] = __builtin_nontemporal_load(gv<u32x2>(d.xlo + off));
     }
   }
 }
@@ -849,10 +861,8 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
     } else {
       unpack8_bf16(in.dir[q], v);
       if (hilo_in) {
-        float l[8];
-        unpack8_bf16(in.lo[q], l);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] += l[e];
+        add4_lo(u32x2{in.dir[q].x, in.dir[q].y}, in.lo[q].x, v);
+        add4_lo(u32x2{in.dir[q].z, in.dir[q].w}, in.lo[q].y, v + 4);
       }
     }
   };
@@ -917,7 +927,7 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
       for (int e = 0; e < 8; ++e) v[e] = fmaf(alpha, xv[e], beta * v[e]);
       if (!last) {
         store8_stream<F32>(xout, off, v);
-        if (write_lo) __builtin_nontemporal_store(lo8_bf16(v), gv<u32x4>(d.xlo + off));
+        if (write_lo) __builtin_nontemporal_store(lo8(v), gv<u32x2>(d.xlo + off));
       } else if (!d.transposed) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = fmaf(-lr_eff, v[e], wrow[q][e]);
