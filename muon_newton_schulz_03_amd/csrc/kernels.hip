@@ -37,6 +37,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Global-memory views of plain pointers.  The pointers in the matrix table are
 // generic; accesses through these views compile to global_* instructions,
@@ -77,29 +79,29 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
 }
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 // Low byte of the (hi, lo) pair that carries X in more precision than one
-// bf16.  hi = bf16(x) is the operand copy itself; lo is x - hi (exact in
-// fp32, at most half a unit in the last place of hi) as a signed count of
-// 1/256 of that unit, rounded to nearest and held in [-127, 127].  hi + lo
-// then holds about 16 significant bits of x.  The unit is 2^(E - 134) for hi's
-// biased exponent E, so lo counts 2^(max(E, 16) - 142); the floor at E = 16
-// (|hi| < 2^-111) keeps both scale factors normal floats.
-__device__ __forceinline__ int lo_exp(uint16_t hi) { return max((int)((hi >> 7) & 0xFF), 16); }
-__device__ __forceinline__ uint32_t lo_byte(float x) {
-  const uint16_t hi = f2bf(x);
-  const float inv = __uint_as_float((uint32_t)(269 - lo_exp(hi)) << 23);  // 2^(142 - E)
-  const float q = rintf(fminf(fmaxf((x - bf2f(hi)) * inv, -127.f), 127.f));
-  return (uint32_t)(int)q & 0xFFu;
+// bf16.  hi = bf16(x) is the operand copy itself.  In the integer order of
+// fp32 bit patterns, x lies within 2^15 of hi (half of bf16's last place is
+// 2^15 fp32 places); lo is that distance in units of 256, rounded to
+// nearest, q = min((bits(x) - bits(hi) + 128) >> 8, 127), stored as a signed
+// byte (the clamp only catches distances within 128 of 2^15).  The pair
+// decodes to the fp32 pattern bits(hi) + 256 q: x to about 16 significant
+// bits (relative error at most 2^-15, unbiased: rounding down in this order
+// would shrink every |x|), in a few integer operations each way.
+__device__ __forceinline__ uint32_t lo_byte(float x, uint32_t hi_bits) {
+  const int r = (int)(__float_as_uint(x) - hi_bits);
+  return (uint32_t)min((r + 128) >> 8, 127) & 0xFFu;
 }
-__device__ __forceinline__ float lo_value(uint16_t hi, uint32_t byte) {
-  const float unit = __uint_as_float((uint32_t)(lo_exp(hi) - 15) << 23);  // 2^(E - 142)
-  return (float)(int)(int8_t)byte * unit;
+__device__ __forceinline__ float with_lo(uint32_t hi_bits, uint32_t lo_word, int e) {
+  const int q = __builtin_amdgcn_sbfe((int)lo_word, 8 * e, 8);
+  return __uint_as_float(hi_bits + ((uint32_t)q << 8));
 }
 
+// Two floats to two bf16 (RNE) in one word, low half first: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+}
 __device__ __forceinline__ u32x2 pack4_bf16(float a, float b, float c, float d) {
-  u32x2 r;
-  r.x = (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
-  r.y = (uint32_t)f2bf(c) | ((uint32_t)f2bf(d) << 16);
-  return r;
+  return u32x2{pack2_bf16(a, b), pack2_bf16(c, d)};
 }
 __device__ __forceinline__ void unpack4_bf16(u32x2 r, float* v) {
   v[0] = __uint_as_float(r.x << 16);
@@ -107,16 +109,28 @@ __device__ __forceinline__ void unpack4_bf16(u32x2 r, float* v) {
   v[2] = __uint_as_float(r.y << 16);
   v[3] = __uint_as_float(r.y & 0xFFFF0000u);
 }
-// Low bytes of 4 values, packed little-endian into one word.
-__device__ __forceinline__ uint32_t pack4_lo(const float* v) {
-  return lo_byte(v[0]) | (lo_byte(v[1]) << 8) | (lo_byte(v[2]) << 16) | (lo_byte(v[3]) << 24);
+// fp32 patterns of the 4 bf16 words packed by pack4_bf16.
+__device__ __forceinline__ void hi_bits4(u32x2 hi, uint32_t* b) {
+  b[0] = hi.x << 16;
+  b[1] = hi.x & 0xFFFF0000u;
+  b[2] = hi.y << 16;
+  b[3] = hi.y & 0xFFFF0000u;
 }
-// v[e] += the low part of element e, given the 4 bf16 hi words (packed as by
-// pack4_bf16) and their 4 low bytes.
-__device__ __forceinline__ void add4_lo(u32x2 hi, uint32_t lo, float* v) {
-  const uint16_t h[4] = {(uint16_t)hi.x, (uint16_t)(hi.x >> 16), (uint16_t)hi.y, (uint16_t)(hi.y >> 16)};
+// Low bytes of 4 values whose bf16 words pack4_bf16 packed into `hi`, packed
+// little-endian into one word.
+__device__ __forceinline__ uint32_t pack4_lo(const float* v, u32x2 hi) {
+  uint32_t b[4];
+  hi_bits4(hi, b);
+  return lo_byte(v[0], b[0]) | (lo_byte(v[1], b[1]) << 8) | (lo_byte(v[2], b[2]) << 16) |
+         (lo_byte(v[3], b[3]) << 24);
+}
+// The 4 values of a (hi, lo) pair: bf16 words packed as by pack4_bf16, low
+// bytes packed as by pack4_lo.
+__device__ __forceinline__ void unpack4_hilo(u32x2 hi, uint32_t lo, float* v) {
+  uint32_t b[4];
+  hi_bits4(hi, b);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] += lo_value(h[e], (lo >> (8 * e)) & 0xFFu);
+  for (int e = 0; e < 4; ++e) v[e] = with_lo(b[e], lo, e);
 }
 
 // LDS row swizzle: 16-byte chunk c of tile row r lives at chunk c ^ swz(r).
@@ -265,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(MomArgs args) {
       const u32x2 h0 = pack4_bf16(xv[q][0], xv[q][1], xv[q][2], xv[q][3]);
       const u32x2 h1 = pack4_bf16(xv[q][4], xv[q][5], xv[q][6], xv[q][7]);
       *gv<u32x4>((uint16_t*)d.xo[0] + xo) = u32x4{h0.x, h0.y, h1.x, h1.y};
-      if (d.xlo) *gv<u32x2>(d.xlo + xo) = u32x2{pack4_lo(xv[q]), pack4_lo(xv[q] + 4)};
+      if (d.xlo) *gv<u32x2>(d.xlo + xo) = u32x2{pack4_lo(xv[q], h0), pack4_lo(xv[q] + 4, h1)};
     }
   }
 
@@ -376,8 +390,10 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs args) {
       u[0] = v.x; u[1] = v.y; u[2] = v.z; u[3] = v.w;
     } else {
       const u32x2 hi = *gv<u32x2>((const uint16_t*)d.xo[0] + xo);
-      unpack4_bf16(hi, u);
-      if (d.xlo) add4_lo(hi, *gv<uint32_t>(d.xlo + xo), u);
+      if (d.xlo)
+        unpack4_hilo(hi, *gv<uint32_t>(d.xlo + xo), u);
+      else
+        unpack4_bf16(hi, u);
     }
     weight_step(d, i, j, u, lr_eff);
   }
@@ -563,12 +579,17 @@ __device__ __forceinline__ void mma_slab(f32x16 (&acc)[2][2], const char* lq, co
 }
 
 // ---- epilogue helpers.  The finished 128x128 tile is staged in LDS as fp32,
-// 16-byte chunk (i, jc) of row i stored at chunk jc ^ cswz(i).  With this
-// swizzle every epilogue access is a conflict-free 16-byte LDS access: the
-// MFMA-layout writes (16 consecutive rows, one chunk), row reads (one row,
-// 16 consecutive chunks) and 4x4-block reads (rows 4L+e, L = 0..15, one chunk).
+// 16-byte chunk (i, jc) of row i (jc = 0..31) stored at chunk
+// jc ^ cswz(i) ^ (jc >> 4).  With this swizzle every epilogue access is a
+// conflict-free 16-byte LDS access: the MFMA-layout writes (16 consecutive
+// rows, one chunk), the row reads of crow8 (16 threads of a row reading
+// chunks 2k, then 2k + 1, k = 0..15: the last term sends chunks 2k and
+// 2k + 16 to different bank groups) and 4x4-block reads (rows 4L+e,
+// L = 0..15, one chunk).
 __device__ __forceinline__ int cswz(int i) { return (i ^ (i >> 2)) & 15; }
-__device__ __forceinline__ float* cptr(float* ct, int i, int j) { return ct + i * kTile + (((j >> 2) ^ cswz(i)) << 2); }
+__device__ __forceinline__ float* cptr(float* ct, int i, int j) {
+  return ct + i * kTile + (((j >> 2) ^ cswz(i) ^ ((j >> 6) & 1)) << 2);
+}
 __device__ __forceinline__ void crow(const float* ct, int r, int c, float* v) {
   f32x4 x = *(const f32x4*)cptr(const_cast<float*>(ct), r, c);
   v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
@@ -579,21 +600,35 @@ __device__ __forceinline__ void cblock(const float* ct, int c, int r, float (&bl
   for (int e = 0; e < 4; ++e) crow(ct, c + e, r, blk[e]);
 }
 
-// Row reads of 8 consecutive columns c..c+7 (c a multiple of 8): chunks c/4 and
-// c/4 + 1.  Each of the two LDS reads takes the even chunk on threads with
-// (c / 8) % 16 < 8 and the odd one on the others, so the 16 threads of a row
-// touch 16 distinct bank groups per read (conflict-free under cswz).
-__device__ __forceinline__ void crow8(const float* ct, int r, int c, float* v) {
-  const int odd_first = (c >> 6) & 1;
-  float a[4], b[4];
-  crow(ct, r, c + 4 * odd_first, a);
-  crow(ct, r, c + 4 - 4 * odd_first, b);
+// Row passes read 8 consecutive columns c..c+7 (c a multiple of 8) of rows
+// rbase + 16 q, q = 0..7: chunks c/4 and c/4 + 1.  cswz(rbase + 16 q) is
+// cswz(rbase) ^ 4 (q & 3), so per thread four base addresses (one per q & 3)
+// serve all passes, the row offset 16 q rows riding in the instruction's
+// immediate offset.
+struct RowReader {
+  const char* row;  // row rbase of the staged tile
+  uint32_t k[8];    // byte offsets of chunks c/4 (k[m]) and c/4 + 1 (k[4 + m]) there, m = q & 3
+  __device__ __forceinline__ RowReader(const float* ct, int rbase, int c) : row((const char*)(ct + rbase * kTile)) {
+    const uint32_t k0 = (uint32_t)((c >> 2) ^ cswz(rbase) ^ ((c >> 6) & 1)) << 4;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    v[e] = odd_first ? b[e] : a[e];
-    v[4 + e] = odd_first ? a[e] : b[e];
+    for (int m = 0; m < 4; ++m) {
+      k[m] = k0 ^ (64u * m);
+      k[4 + m] = k0 ^ (64u * m) ^ 16u;
+    }
   }
-}
+  // v = columns c..c+7 of row rbase + 16 q (q a compile-time constant after unrolling)
+  __device__ __forceinline__ void read(int q, float* v) const {
+    const char* p = row + q * 16 * kTile * 4;
+    const f32x4 x = *(const f32x4*)(p + k[q & 3]);
+    const f32x4 y = *(const f32x4*)(p + k[4 + (q & 3)]);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+  }
+};
+// The MFMA-layout staging write of accumulator chunk (nj, g) of row i:
+// logical chunk 16 wn + 8 nj + 2 g + h (disjoint bits), so with the per-row key
+// cswz(i) ^ 17 wn ^ h the physical chunk is key ^ (8 nj + 2 g).
+__device__ __forceinline__ int stage_key(int i, int wn, int h) { return cswz(i) ^ (17 * wn) ^ h; }
 __device__ __forceinline__ u32x4 pack8_bf16(const float* v) {
   const u32x2 a = pack4_bf16(v[0], v[1], v[2], v[3]), b = pack4_bf16(v[4], v[5], v[6], v[7]);
   return u32x4{a.x, a.y, b.x, b.y};
@@ -602,7 +637,9 @@ __device__ __forceinline__ void unpack8_bf16(u32x4 r, float* v) {
   unpack4_bf16(u32x2{r.x, r.y}, v);
   unpack4_bf16(u32x2{r.z, r.w}, v + 4);
 }
-__device__ __forceinline__ u32x2 lo8(const float* v) { return u32x2{pack4_lo(v), pack4_lo(v + 4)}; }
+__device__ __forceinline__ u32x2 lo8(const float* v, u32x4 hi) {
+  return u32x2{pack4_lo(v, u32x2{hi.x, hi.y}), pack4_lo(v + 4, u32x2{hi.z, hi.w})};
+}
 
 template <bool F32>
 __device__ __forceinline__ void store4(void* base, size_t off, const float* v) {
@@ -843,15 +880,18 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi) {
       const int i = wm * 64 + mi * 32 + (lane & 31);
+      const int key = stage_key(i, wn, h);
+      float* row = ct + i * kTile;
 #pragma unroll
       for (int nj = 0; nj < 2; ++nj)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-          *(f32x4*)cptr(ct, i, wn * 64 + nj * 32 + 8 * g + 4 * h) =
+          *(f32x4*)(row + ((key ^ (8 * nj + 2 * g)) << 2)) =
               f32x4{acc[mi][nj][4 * g], acc[mi][nj][4 * g + 1], acc[mi][nj][4 * g + 2], acc[mi][nj][4 * g + 3]};
     }
   }
   MUON_LDS_BARRIER();
+  const RowReader rows(ct, rbase, c);
 
   auto in_dir = [&](int q, float* v) {  // epilogue input at the direct position of row pass q
     if (F32) {
@@ -859,10 +899,11 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
                                     : (size_t)(i0 + rbase + 16 * q) * d.np + j0 + c;
       load8<true>(STAGE == 2 ? (const void*)d.a : xin, off, v);
     } else {
-      unpack8_bf16(in.dir[q], v);
       if (hilo_in) {
-        add4_lo(u32x2{in.dir[q].x, in.dir[q].y}, in.lo[q].x, v);
-        add4_lo(u32x2{in.dir[q].z, in.dir[q].w}, in.lo[q].y, v + 4);
+        unpack4_hilo(u32x2{in.dir[q].x, in.dir[q].y}, in.lo[q].x, v);
+        unpack4_hilo(u32x2{in.dir[q].z, in.dir[q].w}, in.lo[q].y, v + 4);
+      } else {
+        unpack8_bf16(in.dir[q], v);
       }
     }
   };
@@ -882,7 +923,7 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
         hand_over(q);
         const int r = rbase + 16 * q;
         float v[8];
-        crow8(ct, r, c, v);
+        rows.read(q, v);
         if (kDiag) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -921,13 +962,16 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
       const int r = rbase + 16 * q;
       const size_t off = (size_t)(i0 + r) * d.np + j0 + c;
       float v[8], xv[8];
-      crow8(ct, r, c, v);
+      rows.read(q, v);
       in_dir(q, xv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = fmaf(alpha, xv[e], beta * v[e]);
-      if (!last) {
+      if (!last && !F32) {
+        const u32x4 hi = pack8_bf16(v);
+        __builtin_nontemporal_store(hi, gv<u32x4>((uint16_t*)xout + off));
+        if (write_lo) __builtin_nontemporal_store(lo8(v, hi), gv<u32x2>(d.xlo + off));
+      } else if (!last) {
         store8_stream<F32>(xout, off, v);
-        if (write_lo) __builtin_nontemporal_store(lo8(v), gv<u32x2>(d.xlo + off));
       } else if (!d.transposed) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = fmaf(-lr_eff, v[e], wrow[q][e]);

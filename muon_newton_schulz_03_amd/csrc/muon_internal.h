@@ -30,7 +30,7 @@ struct DevMat {
   void* w;            // weights (rows x cols), f32 or bf16
   const void* g;      // gradient (rows x cols), f32 or bf16
   float* mom;         // momentum (rows x cols), f32
-  uint8_t* xlo;       // bf16 path: low byte of X, X - bf16(X) in 1/256 units of bf16(X)'s last place (mp x np); else null
+  uint8_t* xlo;       // bf16 path: low byte of X (the rounded fp32-pattern distance to bf16(X) / 256, mp x np); else null
   void* xo[2];        // operand copies of X (ping-pong), bf16 or f32, mp x np
   void* a;            // A = X X^T, mp x mp (bf16 or f32)
   void* b;            // B = b A + c A A, mp x mp
