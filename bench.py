@@ -46,9 +46,9 @@ def work_model(shapes, T):
 
 
 def momentum_bytes(shapes, master: bool):
-    """Algorithmic HBM bytes of the momentum kernel: G (bf16) + M read/write + X0 (bf16 [+ bf16 low word])."""
+    """Algorithmic HBM bytes of the momentum kernel: G (bf16) + M read/write + X0 (bf16 [+ its low byte])."""
     p = sum(r * c for r, c in shapes)
-    return p * (2 + 4 + 4 + 2 + (2 if master else 0))
+    return p * (2 + 4 + 4 + 2 + (1 if master else 0))
 
 
 def read_profile_value(summary: str, key: str):

@@ -23,7 +23,7 @@ def test_work_model_matches_oracle_counts():
     assert w["dense_step"] == sum(O.ns_flops_dense(r, c, wl.T) for r, c in wl.shapes)
     assert abs(w["step"] - 1.1422e12) / 1.1422e12 < 1e-3
     assert w["update"] == 130_459_631_616  # 48 * 2 * 768^3 + 24 * 2 * 768^2 * 3072
-    assert bench.momentum_bytes(wl.shapes, True) == wl.params * 14
+    assert bench.momentum_bytes(wl.shapes, True) == wl.params * 13
 
 
 def test_profile_summaries_are_text_with_commands():
