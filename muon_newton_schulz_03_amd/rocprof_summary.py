@@ -40,7 +40,6 @@ KINDS = {
     "ns_stage_kernel<1": "gram",
     "ns_stage_kernel<2": "poly",
     "ns_stage_kernel<3": "update",
-    "ns_update_kernel": "update",
     "apply_kernel": "apply",
 }
 
