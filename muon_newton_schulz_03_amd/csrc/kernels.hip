@@ -799,6 +799,8 @@ constexpr int kHiLo = 1, kLast = 2, kWriteLo = 4;
 struct EpiIn {
   u32x4 dir[8];  // bf16 at the direct positions (A of stage 2, X of stage 3)
   u32x2 lo[8];   // low bytes of X (stage 3, kHiLo)
+  f32x4 w[16];   // W of the weight step (stage 3, kLast): row pass q at w[2q], w[2q + 1];
+                 // transposed W: row j0 + 4 rb4 + 32 (q >> 2) + (q & 3) of the column passes at w[q]
 };
 
 template <int STAGE, bool F32, int MODE>
@@ -817,6 +819,25 @@ __device__ __forceinline__ void epi_prefetch(const StageArgs& args, const DevMat
       const size_t off = (size_t)(o.i0 + rbase + 16 * q) * d.np + o.j0 + c;
       in.dir[q] = *gv<u32x4>((const uint16_t*)xin + off);
       if (MODE & kHiLo) in.lo[q] = __builtin_nontemporal_load(gv<u32x2>(d.xlo + off));
+    }
+    if (MODE & kLast) {  // W, so that its latency hides behind the last slab
+      float t[4];
+      if (!d.transposed) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            weight_load(d, o.i0 + rbase + 16 * q, o.j0 + c + 4 * h, t);
+            in.w[2 * q + h] = f32x4{t[0], t[1], t[2], t[3]};
+          }
+      } else if (o.j0 < d.n) {
+        const int c4 = 4 * (tid & 31), rb4 = tid >> 5;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          weight_load_rows(d, o.j0 + 4 * rb4 + 32 * (q >> 2) + (q & 3), o.i0 + c4, t);
+          in.w[q] = f32x4{t[0], t[1], t[2], t[3]};
+        }
+      }
     }
   }
 }
@@ -948,8 +969,8 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
     else
       direct(std::false_type{});
   } else {
-    float wrow[8][8];
-    if (last && !d.transposed) {
+    float wrow[8][8];  // fp32 path (bf16 operands take W from the prefetched inputs)
+    if (F32 && last && !d.transposed) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         weight_load(d, i0 + rbase + 16 * q, j0 + c, wrow[q]);
@@ -974,7 +995,7 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
         store8_stream<F32>(xout, off, v);
       } else if (!d.transposed) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = fmaf(-lr_eff, v[e], wrow[q][e]);
+        for (int e = 0; e < 8; ++e) v[e] = fmaf(-lr_eff, v[e], F32 ? wrow[q][e] : in.w[2 * q + (e >> 2)][e & 3]);
         weight_store(d, i0 + r, j0 + c, v);
         weight_store(d, i0 + r, j0 + c + 4, v + 4);
       } else {
@@ -985,9 +1006,11 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
     }
     if (last && d.transposed && j0 < d.n) {
       // W is the transpose of the canonical X: W row (j0 + R) holds O[i0 + c..][j0 + R]
-      float wv[16][4];
+      float wv[16][4];  // fp32 path (bf16 operands take W from the prefetched inputs)
+      if (F32) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) weight_load_rows(d, j0 + 4 * rb4 + 32 * (q >> 2) + (q & 3), i0 + c4, wv[q]);
+        for (int q = 0; q < 16; ++q) weight_load_rows(d, j0 + 4 * rb4 + 32 * (q >> 2) + (q & 3), i0 + c4, wv[q]);
+      }
       MUON_LDS_BARRIER();
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) {
@@ -998,7 +1021,7 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
         for (int f = 0; f < 4; ++f) {
           float w[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = fmaf(-lr_eff, blk[e][f], wv[4 * qb + f][e]);
+          for (int e = 0; e < 4; ++e) w[e] = fmaf(-lr_eff, blk[e][f], F32 ? wv[4 * qb + f][e] : in.w[4 * qb + f][e]);
           weight_store_rows(d, j0 + r + f, i0 + c4, w);
         }
       }
