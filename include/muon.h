@@ -25,8 +25,10 @@
  * Precision.  MUON_PATH_BF16: the three products take bf16 operands (rounded
  * to nearest even) and accumulate in fp32; A and B are stored bf16; the a*X
  * term reads X for the first `x_master_iters` iterations (default 3) as a
- * hi/lo pair of bf16 words (hi = bf16(X), the operand copy; lo = bf16(X - hi);
- * about 16 significant bits) and as the bf16 copy alone afterwards.  Matrices whose short side is
+ * (hi, lo) pair, hi = bf16(X) (the operand copy) and lo one signed byte: the
+ * distance from hi to X in the integer order of fp32 bit patterns, in units
+ * of 256, rounded (about 16 significant bits, relative error <= 2^-15), and as
+ * the bf16 copy alone afterwards.  Matrices whose short side is
  * below 64 take the fp32 arithmetic even on this path: their A*A and B*X
  * contractions are too short for bf16 rounding errors to average out.
  * MUON_PATH_F32: everything fp32.
@@ -96,8 +98,9 @@ typedef struct muon_matrix_desc {
  * max_T 64, 2 groups. */
 typedef struct muon_options {
   int32_t path;           /* MUON_PATH_BF16 or MUON_PATH_F32 */
-  int32_t x_master_iters; /* bf16 path: iterations 1..k read X in a*X as a hi/lo
-                             bf16 pair; < 0 selects the default 3; ignored on f32 */
+  int32_t x_master_iters; /* bf16 path: iterations 1..k read X in a*X as its
+                             (bf16, low byte) pair; < 0 selects the default 3;
+                             ignored on f32 */
   int32_t zero_momentum;  /* != 0: muon_init zeroes every momentum buffer */
   int32_t max_T;          /* largest T muon_step accepts; <= 0 selects 64 */
   int32_t groups;         /* 1: every launch on the caller's stream; 2 (or <= 0,

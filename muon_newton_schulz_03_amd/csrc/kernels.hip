@@ -783,14 +783,14 @@ __device__ __forceinline__ bool dma_operand(char* lds, const char* base, uint32_
 
 // Inputs of a tile's epilogue, prefetched while its last K slab multiplies
 // (bf16 products): A at the direct positions (stage 2), X (stage 3: its
-// bf16 copy, plus the low words in the kHiLo variant).  Global stores share the in-order
+// bf16 copy, plus the low bytes in the kHiLo variant).  Global stores share the in-order
 // vector-memory counter with loads, so every load of the epilogue is issued
 // before its first store.  Row pass: thread handles tile rows (tid >> 4) + 16 q
 // and columns c..c+7 (16-byte bf16 accesses); column pass: the 4x4 block
 // C[c..c+3][r..r+3] with c = 4 (tid & 31), r = 4 (tid >> 5) + 32 q, written
 // as 4 rows of the transposed tile.
 // Stage 3 kernels come in variants: kHiLo (the a*X term reads X as its
-// hi/lo bf16 pair), kWriteLo (the new X is written as a hi/lo pair too) and
+// (bf16, low byte) pair), kWriteLo (the new X is written as such a pair too) and
 // kLast (last iteration: the weight step instead of storing X).  Keeping the
 // epilogue's store count a compile-time constant lets the compiler's waits for
 // the prefetched inputs leave the earlier row passes' stores in flight.

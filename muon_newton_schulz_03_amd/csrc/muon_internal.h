@@ -64,7 +64,7 @@ struct StageArgs {
   int32_t ntiles;   // table length (persistent blocks stride through it)
   int32_t t;        // iteration, 1-based
   int32_t T;        // iterations this step
-  int32_t kmaster;  // bf16 path: iterations 1..kmaster read X as its hi/lo bf16 pair in a*X
+  int32_t kmaster;  // bf16 path: iterations 1..kmaster read X as its (bf16, low byte) pair in a*X
   float a, b, c;
   float lr;
 };

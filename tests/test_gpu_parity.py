@@ -281,7 +281,7 @@ def test_profile_counts():
 
 @pytest.mark.parametrize("k", [0, 5])
 def test_master_copy_settings(k):
-    """x_master_iters = 0 (bf16 X throughout) and 5 (hi/lo pair every iteration) also pass."""
+    """x_master_iters = 0 (bf16 X throughout) and 5 (the (bf16, low byte) pair every iteration) also pass."""
     say(f"[gpu] x_master_iters={k}")
     shapes = [(768, 768)] * 2 + [(768, 3072)]
     steps = [[inputs.custom_gradient(r, c, 60 + i, std=0.02) for i, (r, c) in enumerate(shapes)]]
