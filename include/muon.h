@@ -8,8 +8,8 @@
  *     Tuning": Muon is applied to hidden-layer matrix weights only; the update
  *     is orthogonalised after a Nesterov momentum step.
  *   - Overview page "The NanoGPT speedrun", paragraph "Six records account for
- *     most of the speedup" (record #3): the momentum update is replaced by its
- *     nearest semi-orthogonal matrix through five Newton-Schulz steps.
+ *     most of the speedup" (record #3): the momentum update is orthogonalised
+ *     (approximately its polar factor U V^T) by five Newton-Schulz steps.
  *
  * What muon_step computes, per matrix (rows x cols, row-major):
  *   M <- fl32(mu*M + G)                       momentum, fp32 buffer, in place

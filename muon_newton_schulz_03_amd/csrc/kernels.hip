@@ -3,8 +3,9 @@
 // The method (guide page "NanoGPT Speedrun: The Ultimate Guide ...", section
 // "Optimizer and Training Strategy Tuning"; overview page "The NanoGPT
 // speedrun", paragraph "Six records account for most of the speedup"):
-// Nesterov momentum, then replace the update by its nearest semi-orthogonal
-// matrix via Newton-Schulz steps, then apply it to the weights.
+// Nesterov momentum, then orthogonalise the update with a few Newton-Schulz
+// iterations (an approximation of U V^T from its SVD), then apply it to the
+// weights.
 //
 //   momentum_kernel    M <- mu M + G (one fp32 rounding), U = G + mu M or M,
 //                      per-tile partial sums of U^2, X0 = U written in the
@@ -582,7 +583,7 @@ __device__ __forceinline__ void mma_slab(f32x16 (&acc)[2][2], const char* lq, co
 // 16-byte chunk (i, jc) of row i (jc = 0..31) stored at chunk
 // jc ^ cswz(i) ^ (jc >> 4).  With this swizzle every epilogue access is a
 // conflict-free 16-byte LDS access: the MFMA-layout writes (16 consecutive
-// rows, one chunk), the row reads of crow8 (16 threads of a row reading
+// rows, one chunk), the row reads of RowReader (16 threads of a row reading
 // chunks 2k, then 2k + 1, k = 0..15: the last term sends chunks 2k and
 // 2k + 16 to different bank groups) and 4x4-block reads (rows 4L+e,
 // L = 0..15, one chunk).
@@ -783,7 +784,8 @@ __device__ __forceinline__ bool dma_operand(char* lds, const char* base, uint32_
 
 // Inputs of a tile's epilogue, prefetched while its last K slab multiplies
 // (bf16 products): A at the direct positions (stage 2), X (stage 3: its
-// bf16 copy, plus the low bytes in the kHiLo variant).  Global stores share the in-order
+// bf16 copy, plus the low bytes in the kHiLo variant) and W (kLast: the
+// weight step's other input).  Global stores share the in-order
 // vector-memory counter with loads, so every load of the epilogue is issued
 // before its first store.  Row pass: thread handles tile rows (tid >> 4) + 16 q
 // and columns c..c+7 (16-byte bf16 accesses); column pass: the 4x4 block

@@ -11,8 +11,9 @@ pages give the method:
    ("NanoGPT Speedrun: The Ultimate Guide ...", section "Optimizer and
    Training Strategy Tuning": Muon orthogonalises the update after a Nesterov
    momentum step, and only for hidden-layer matrices);
-2. replace that update by an approximation of its nearest semi-orthogonal
-   matrix, computed with five Newton-Schulz steps
+2. replace that update by an approximation of its polar factor U V^T (the
+   closest matrix with orthonormal rows or columns), computed with five
+   Newton-Schulz steps
    ("The NanoGPT speedrun", paragraph "Six records account for most of the
    speedup", record #3);
 3. scale the result and subtract it from the weights.
@@ -95,7 +96,7 @@ def newton_schulz(X0: np.ndarray, a: float, b: float, c: float, T: int) -> np.nd
     """T quintic Newton-Schulz steps on a short-side-first X_0 (rows <= cols).
 
     Speedrun overview page, "Six records ..." (record #3): the normalised update
-    is driven towards its nearest semi-orthogonal matrix by Newton-Schulz
+    is driven towards its polar factor U V^T by Newton-Schulz
     steps.  Each step: A = X X^T, B = b A + c A A, X <- a X + B X.
     """
     a, b, c = f32(a), f32(b), f32(c)

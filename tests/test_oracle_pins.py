@@ -204,7 +204,7 @@ def test_singular_value_band():
     assert sv.min() >= 0.68183 - 1e-6 and sv.max() <= 1.20237 + 1e-6
 
 
-# --- P7: steepest descent under the spectral norm ---------------------------
+# --- P7: the polar factor maximises <G, O> over the spectral-norm unit ball --
 
 def test_polar_attains_nuclear_norm():
     # overview page, "Reading guide": the orthogonalised update is steepest
