@@ -1114,16 +1114,21 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void ns_stage_kernel(StageA
   // the X layout for k < qt * 128, P for k < pt * 128 (stage 2, qt <= pt) or
   // always (stage 3, X itself).
   constexpr bool kSymQ = STAGE >= 2, kSymP = STAGE == 2;
+  // A diagonal tile of the symmetric products (stages 1 and 2) has the same
+  // panel, in the same layout, as both operands: its slabs are loaded once,
+  // into the Q half, and the P fragments are read from there too.
   auto issue = [&](const TileOps& op, int kt) {
     char* lq = smem + (kt & 1) * kSlabLds;
     dma_operand<F32>(lq, op.q, op.qld, op.qt, kSymQ, false, kt, w, lane);
-    dma_operand<F32>(lq + kTile * 128, op.p, op.pld, op.pt, kSymP, STAGE == 3, kt, w, lane);
+    if (STAGE == 3 || !op.diag)
+      dma_operand<F32>(lq + kTile * 128, op.p, op.pld, op.pt, kSymP, STAGE == 3, kt, w, lane);
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
 
   DevMat d = load_stage_mat<STAGE, MODE>(args.mats + tl.mat);
   TileOps o = tile_ops<STAGE, F32>(args, d, tl);
+  auto p_half = [&](const char* lq) { return (STAGE <= 2 && o.diag) ? lq : lq + kTile * 128; };
   int pend = 0;  // vector-memory operations issued after the request of this tile's slab 0
   issue(o, 0);
   for (;;) {
@@ -1152,7 +1157,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void ns_stage_kernel(StageA
         MUON_LDS_BARRIER();    // ... everyone's, and slab kt - 1 is no longer read
         issue(o, kt + 1);
         const char* lq = smem + (kt & 1) * kSlabLds;
-        mma_slab<F32, decltype(qx)::value, decltype(px)::value>(acc, lq, lq + kTile * 128, wm, wn, lane);
+        mma_slab<F32, decltype(qx)::value, decltype(px)::value>(acc, lq, p_half(lq), wm, wn, lane);
       }
     };
     const int nlast = o.nk - 1;
@@ -1192,7 +1197,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void ns_stage_kernel(StageA
       MUON_LDS_BARRIER();
       epi_prefetch<STAGE, F32, MODE>(args, d, o, in, tid);
       const char* lq = smem + (nlast & 1) * kSlabLds;
-      mma_slab<F32, false, STAGE == 3>(acc, lq, lq + kTile * 128, wm, wn, lane);
+      mma_slab<F32, false, STAGE == 3>(acc, lq, p_half(lq), wm, wn, lane);
     }
     MUON_LDS_BARRIER();  // the last slab has been read by all: LDS holds the staged tile next
     tile_epilogue<STAGE, F32, MODE>(args, d, o, acc, in, (float*)smem, tid, lane, wm, wn, [&] {
