@@ -195,15 +195,16 @@ typedef struct muon_plan_info {
 int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts,
                   muon_plan_info* info, int kind, int32_t* tiles, int tile_cap, int32_t* n_tiles);
 
-/* Per-launch timing with HIP events recorded around the launches of
- * muon_step (enable != 0 turns it on; it adds event records to the stream).
- * muon_profile_select restricts the timed launches to the kinds whose bit
- * (1 << MUON_KIND_*) is set in kind_mask (default: all kinds); each event
- * record costs the stream a few microseconds, so timing only the kind of
- * interest disturbs the step least.  muon_profile_read waits for the
- * recorded events, adds their durations per kind into ms[MUON_KIND_COUNT]
- * and launches[MUON_KIND_COUNT] (totals since the last read), and resets
- * the totals. */
+/* Per-launch timing with HIP events (enable != 0 turns it on).  Each timed
+ * launch of muon_step is issued with hipExtLaunchKernel and an event pair
+ * that takes the dispatch's own start and end times, so timing adds no
+ * event records to the stream; it does add host work per launch, and a step
+ * with timing on must not be captured in a graph.  muon_profile_select
+ * restricts the timed launches to the kinds whose bit (1 << MUON_KIND_*) is
+ * set in kind_mask (default: all kinds).  muon_profile_read waits for the
+ * events, adds their durations per kind into ms[MUON_KIND_COUNT] and
+ * launches[MUON_KIND_COUNT] (totals since the last read), and resets the
+ * totals. */
 int muon_profile_enable(muon_plan* plan, int enable);
 int muon_profile_select(muon_plan* plan, uint32_t kind_mask);
 int muon_profile_read(muon_plan* plan, double* ms, int64_t* launches);

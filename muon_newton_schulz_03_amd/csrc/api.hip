@@ -15,11 +15,12 @@
 #include "muon_internal.h"
 
 namespace muon {
-hipError_t launch_momentum(const MomArgs& args, int blocks, hipStream_t stream);
-hipError_t launch_apply(const ApplyArgs& args, int blocks, hipStream_t stream);
-hipError_t launch_stage(int stage, bool f32, const StageArgs& args, int blocks, hipStream_t stream);
+hipError_t launch_momentum(const MomArgs& args, int blocks, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_apply(const ApplyArgs& args, int blocks, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_stage(int stage, bool f32, const StageArgs& args, int blocks, hipStream_t stream, hipEvent_t ev0,
+                        hipEvent_t ev1);
 hipError_t prepare_stage_kernels();
-hipError_t launch_norm(const DevMat* mats, int n, hipStream_t stream);
+hipError_t launch_norm(const DevMat* mats, int n, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 }  // namespace muon
 
 using namespace muon;
@@ -431,31 +432,29 @@ int note_slot_use(muon_plan* p, hipStream_t stream) {
   return MUON_OK;
 }
 
-constexpr size_t kNoProfile = ~(size_t)0;
+// The event pair that times one launch, or null events when the launch is not
+// profiled.  The launch records them itself (they take the dispatch's own
+// start and end times), so profiling adds nothing to the stream.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
 
-int prof_begin(muon_plan* p, int kind, hipStream_t stream, size_t* idx) {
-  *idx = kNoProfile;
+int prof_events(muon_plan* p, int kind, LaunchEvents* ev) {
+  *ev = LaunchEvents{};
   if (!p->prof || !((p->pmask >> kind) & 1u)) return MUON_OK;
   if (p->pused * 2 + 2 > p->pev.size()) {
     for (int k = 0; k < 64; ++k) {
-      hipEvent_t ev;
-      hipError_t e = hipEventCreate(&ev);
-      if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
-      p->pev.push_back(ev);
+      hipEvent_t e;
+      hipError_t err = hipEventCreate(&e);
+      if (err != hipSuccess) return hip_fail(err, "hipEventCreate");
+      p->pev.push_back(e);
     }
   }
-  *idx = p->pused++;
+  const size_t idx = p->pused++;
   if (p->pkind.size() < p->pused) p->pkind.resize(p->pused);
-  p->pkind[*idx] = kind;
-  hipError_t e = hipEventRecord(p->pev[2 * *idx], stream);
-  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(profile)");
-  return MUON_OK;
-}
-
-int prof_end(muon_plan* p, hipStream_t stream, size_t idx) {
-  if (!p->prof || idx == kNoProfile) return MUON_OK;
-  hipError_t e = hipEventRecord(p->pev[2 * idx + 1], stream);
-  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(profile)");
+  p->pkind[idx] = kind;
+  ev->start = p->pev[2 * idx];
+  ev->stop = p->pev[2 * idx + 1];
   return MUON_OK;
 }
 
@@ -705,7 +704,7 @@ static int step_impl(muon_plan* p, const muon_matrix_desc* descs, int n, const f
   const DevMat* mats = slot_ptr(p, p->slot);
   static const int kKinds[3] = {MUON_KIND_GRAM, MUON_KIND_POLY, MUON_KIND_UPDATE};
   static const char* kNames[3] = {"gram launch", "poly launch", "update launch"};
-  size_t pi = 0;
+  LaunchEvents ev;
   int rc;
 
   // Each group's whole step (momentum, norm, T iterations) runs on a stream of
@@ -737,19 +736,16 @@ static int step_impl(muon_plan* p, const muon_matrix_desc* descs, int n, const f
       const Tile* mom_tiles = (const Tile*)(p->ws + p->lay.mom_tiles[grp]);
       const int nmom = (int)p->tab.mom[grp].size();
       MomArgs ma{mats, mom_tiles, momentum, nesterov ? 1 : 0};
-      if ((rc = prof_begin(p, MUON_KIND_MOMENTUM, s, &pi))) return rc;
-      if ((rc = check_launch(launch_momentum(ma, nmom, s), "momentum launch"))) return rc;
-      if ((rc = prof_end(p, s, pi))) return rc;
+      if ((rc = prof_events(p, MUON_KIND_MOMENTUM, &ev))) return rc;
+      if ((rc = check_launch(launch_momentum(ma, nmom, s, ev.start, ev.stop), "momentum launch"))) return rc;
       if (T == 0) {
         ApplyArgs aa{mats, mom_tiles, lr};
-        if ((rc = prof_begin(p, MUON_KIND_APPLY, s, &pi))) return rc;
-        if ((rc = check_launch(launch_apply(aa, nmom, s), "apply launch"))) return rc;
-        if ((rc = prof_end(p, s, pi))) return rc;
+        if ((rc = prof_events(p, MUON_KIND_APPLY, &ev))) return rc;
+        if ((rc = check_launch(launch_apply(aa, nmom, s, ev.start, ev.stop), "apply launch"))) return rc;
       } else {
         const int f0 = p->tab.first[grp], nf = p->tab.first[grp + 1] - f0;
-        if ((rc = prof_begin(p, MUON_KIND_NORM, s, &pi))) return rc;
-        if ((rc = check_launch(launch_norm(mats + f0, nf, s), "norm launch"))) return rc;
-        if ((rc = prof_end(p, s, pi))) return rc;
+        if ((rc = prof_events(p, MUON_KIND_NORM, &ev))) return rc;
+        if ((rc = check_launch(launch_norm(mats + f0, nf, s, ev.start, ev.stop), "norm launch"))) return rc;
       }
       return MUON_OK;
     }
@@ -763,9 +759,8 @@ static int step_impl(muon_plan* p, const muon_matrix_desc* descs, int n, const f
       // the stride the table was laid out for, or fewer blocks when the
       // table is shorter (a multiple of 8: every block keeps its XCD)
       const int grid = std::min((ntab + 7) / 8 * 8, kProductGrid);
-      if ((rc = prof_begin(p, kKinds[k], s, &pi))) return rc;
-      if ((rc = check_launch(launch_stage(k + 1, prec == 1, sa, grid, s), kNames[k]))) return rc;
-      if ((rc = prof_end(p, s, pi))) return rc;
+      if ((rc = prof_events(p, kKinds[k], &ev))) return rc;
+      if ((rc = check_launch(launch_stage(k + 1, prec == 1, sa, grid, s, ev.start, ev.stop), kNames[k]))) return rc;
     }
     return MUON_OK;
   };

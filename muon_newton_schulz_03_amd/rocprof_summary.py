@@ -4,7 +4,12 @@ Two summaries:
 
 * kernel statistics from ``rocprofv3 --kernel-trace --stats --output-format csv``
   (``*_kernel_stats.csv`` and ``*_kernel_trace.csv``): per-kernel calls and
-  average durations, plus the per-dispatch durations of the product kernels;
+  average durations over the whole run; the mean duration per kind over the
+  dispatches of bench.py's timed region (its last ``--steps`` steps; a step
+  starts with the momentum pass of each matrix group, each followed by its
+  norm or apply dispatch), beside what bench.py's own HIP
+  events gave for its timed kernel in the same run (read from its JSON line
+  in ``bench_log``, when given); the per-dispatch durations of the last step;
 * HBM traffic from two ``--pmc`` runs (``FETCH_SIZE``, then ``WRITE_SIZE``,
   KiB per dispatch) of ``bench.py --calibrate-copy``, scaled by what the same
   counters read for the plain copy kernel of known size that run contains;
@@ -16,7 +21,7 @@ Two summaries:
   1024 FLOP must equal its known FLOPs, and the clock GRBM_GUI_ACTIVE / 8 /
   dispatch time must stay within the chip's 2.4 GHz.
 
-    python -m muon_newton_schulz_03_amd.rocprof_summary stats  <trace_dir> <out.txt> "<command>"
+    python -m muon_newton_schulz_03_amd.rocprof_summary stats  <trace_dir> <out.txt> "<command>" [bench_log]
     python -m muon_newton_schulz_03_amd.rocprof_summary traffic <fetch_dir> <write_dir> <out.txt> "<commands>"
     python -m muon_newton_schulz_03_amd.rocprof_summary mfma    <pmc_dir> <out.txt> "<command>"
 """
@@ -25,6 +30,7 @@ from __future__ import annotations
 import csv
 import glob
 import hashlib
+import json
 import os
 import sys
 from collections import defaultdict
@@ -66,7 +72,20 @@ def _one(pattern: str) -> str:
     return hits[0]
 
 
-def stats_summary(trace_dir: str, command: str) -> str:
+def _timed_steps(command: str) -> int:
+    words = command.split()
+    return int(words[words.index("--steps") + 1]) if "--steps" in words else 0
+
+
+def _bench_line(bench_log: str):
+    with open(bench_log) as f:
+        for line in f:
+            if line.startswith("{"):
+                return json.loads(line)
+    return None
+
+
+def stats_summary(trace_dir: str, command: str, bench_log: str | None = None) -> str:
     stats = list(csv.DictReader(open(_one(os.path.join(trace_dir, "**", "*kernel_stats.csv")))))
     trace = list(csv.DictReader(open(_one(os.path.join(trace_dir, "**", "*kernel_trace.csv")))))
     lines = ["# rocprofv3 kernel statistics, Muon step on the GPT-2 small hidden set (72 matrices, T = 5)",
@@ -87,14 +106,30 @@ def stats_summary(trace_dir: str, command: str) -> str:
         a[4] = r["Name"]
     for (k, name), (calls, tot, mn, mx, _) in sorted(agg.items()):
         lines.append(f"{k:10s} {calls:7d} {tot / calls:9.1f} {mn:9.1f} {mx:9.1f}   {name[:70]}")
-    lines.append("# per-dispatch durations (us) of the last step, in launch order")
     mu = [r for r in trace if kind_of(r["Kernel_Name"])]
-    last = []
-    for r in reversed(mu):
-        last.append(r)
-        if kind_of(r["Kernel_Name"]) == "momentum":
-            break
-    for r in reversed(last):
+    mu.sort(key=lambda r: int(r["Dispatch_Id"]) if "Dispatch_Id" in r else 0)
+    # step starts: a momentum dispatch not preceded by another group's momentum
+    # pass (momentum, then norm or apply)
+    head = ("momentum", "norm", "apply")
+    starts = [i for i, r in enumerate(mu)
+              if kind_of(r["Kernel_Name"]) == "momentum" and (i == 0 or kind_of(mu[i - 1]["Kernel_Name"]) not in head)]
+    steps = _timed_steps(command)
+    if steps:
+        region = mu[starts[-steps]:] if len(starts) >= steps else []
+        per = defaultdict(list)
+        for r in region:
+            per[kind_of(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+        lines.append(f"# timed region: the last {steps} steps of the run; kind, dispatches, mean_us")
+        for k in sorted(per):
+            lines.append(f"timed_{k:10s} {len(per[k]):5d} {sum(per[k]) / len(per[k]):9.1f}")
+    if bench_log:
+        d = _bench_line(bench_log)
+        if d and "roofline" in d:
+            r = d["roofline"]
+            lines.append(f"# bench.py in the same run, HIP events on its timed kernel ({r['kernel']}): "
+                         f"{1000.0 * r['ms_per_launch']:.1f} us per launch, {d['ms_per_step']:.4f} ms per step")
+    lines.append("# per-dispatch durations (us) of the last step, in launch order")
+    for r in mu[starts[-1]:] if starts else []:
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
         lines.append(f"  {kind_of(r['Kernel_Name']):10s} {dur:9.1f}   {r['Kernel_Name'][:70]}")
     return "\n".join(lines) + "\n"
@@ -193,7 +228,7 @@ def mfma_summary(pmc_dir: str, command: str) -> str:
 
 def main(argv):
     if argv[0] == "stats":
-        text = stats_summary(argv[1], argv[3])
+        text = stats_summary(argv[1], argv[3], argv[4] if len(argv) > 4 else None)
         out = argv[2]
     elif argv[0] == "traffic":
         text = traffic_summary(argv[1], argv[2], argv[4])

@@ -107,3 +107,39 @@ def test_bench_reads_values_only_for_the_current_sources(tmp_path, monkeypatch):
     assert bench.read_traffic("gram") is None  # no such line
     path.write_text("kernel_source_hash = 0000000000000000\nupdate_hbm_bytes_per_launch = 123\n")
     assert bench.read_traffic("update") is None  # kernels changed since the counters were taken
+
+
+def test_timed_region_means_and_bench_figure(tmp_path):
+    """Two matrix groups: a step opens with (momentum, norm) per group; the timed
+    region is the last --steps steps, and its per-kind means use those
+    dispatches only."""
+    names = {"mom": "muon::momentum_kernel(muon::MomArgs)", "norm": "muon::norm_kernel(muon::DevMat const*)",
+             "gram": "void muon::ns_stage_kernel<1, false, 0>(muon::StageArgs)",
+             "upd": "void muon::ns_stage_kernel<3, false, 5>(muon::StageArgs)"}
+    rows, t, did = [], 0, 0
+
+    def step(gram_us, upd_us):
+        nonlocal t, did
+        for k, us in (("mom", 100), ("norm", 5), ("mom", 100), ("norm", 5),
+                      ("gram", gram_us), ("gram", gram_us), ("upd", upd_us), ("upd", upd_us + 20)):
+            did += 1
+            rows.append((did, names[k], t, t + us * 1000))
+            t += us * 1000 + 1000
+    step(500, 900)  # a warm-up step: slow, outside the timed region
+    step(90, 150)
+    step(110, 170)
+    write_csv(str(tmp_path / "s" / "run_kernel_trace.csv"), ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"],
+              list(reversed(rows)))  # file order does not matter: dispatches are sorted by id
+    write_csv(str(tmp_path / "s" / "run_kernel_stats.csv"), ["Name", "Calls", "TotalDurationNs", "MinNs", "MaxNs"],
+              [(names["gram"], 6, 1, 1, 1)])
+    log = tmp_path / "bench.log"
+    log.write_text('[bench] text\n{"ms_per_step": 1.5, "roofline": {"kernel": "update", "ms_per_launch": 0.171}}\n')
+    text = R.stats_summary(str(tmp_path / "s"), "rocprofv3 -- python bench.py --steps 2 --warmup 1", str(log))
+    timed = {ln.split()[0]: ln.split()[1:] for ln in text.splitlines() if ln.startswith("timed_")}
+    assert timed["timed_gram"] == ["4", "100.0"]
+    assert timed["timed_update"] == ["4", "170.0"]  # (150 + 170 + 170 + 190) / 4
+    assert timed["timed_momentum"] == ["4", "100.0"]
+    assert "update): 171.0 us per launch, 1.5000 ms per step" in text
+    # the last step, from the first group's momentum pass on
+    tail = text.split("in launch order\n")[1].split("\n")
+    assert [ln.split()[0] for ln in tail if ln] == ["momentum", "norm", "momentum", "norm", "gram", "gram", "update", "update"]
