@@ -875,13 +875,16 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
   const int c4 = 4 * (tid & 31), rb4 = tid >> 5;     // 4x4-block (column) passes
   const int i0 = o.i0, j0 = o.j0;
 
-  float pre = 1.f;  // stage 1 of the first iteration works on U: A = s^2 U U^T
-  // the norm scale through a scalar load: a vector load here would wait for the prefetched inputs
-  if (STAGE == 1 && t == 1) pre = load_uniform(d.sc) * load_uniform(d.sc);
-  float alpha = args.a, beta = 1.f;
-  if (STAGE == 3 && t == 1) {
-    beta = load_uniform(d.sc);
-    alpha = args.a * beta;
+  // The first iteration works on U = X0 / s (s = 1 / (||U||_F + eps)): A = s^2 U U^T,
+  // and B is stored as s B, so that the update's product (s B) U is B X0 and
+  // only its a X0 term needs s.  The norm scale comes through a scalar load: a
+  // vector load here would wait for the prefetched inputs.
+  float pre = 1.f, cb = args.b, cc = args.c, alpha = args.a;
+  if (t == 1) {
+    const float s = load_uniform(d.sc);
+    if (STAGE == 1) pre = s * s;
+    if (STAGE == 2) cb *= s, cc *= s;
+    if (STAGE == 3) alpha *= s;
   }
   constexpr bool last = STAGE == 3 && (MODE & kLast);
   constexpr bool hilo_in = STAGE == 3 && !F32 && (MODE & kHiLo);
@@ -962,7 +965,7 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
           float av[8];
           in_dir(q, av);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = fmaf(args.c, v[e], args.b * av[e]);
+          for (int e = 0; e < 8; ++e) v[e] = fmaf(cc, v[e], cb * av[e]);
         }
         store8<F32>(sym_out, (size_t)(i0 + r) * d.mp + j0 + c, v);
       }
@@ -989,7 +992,7 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
       rows.read(q, v);
       in_dir(q, xv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = fmaf(alpha, xv[e], beta * v[e]);
+      for (int e = 0; e < 8; ++e) v[e] = fmaf(alpha, xv[e], v[e]);
       if (!last && !F32) {
         const u32x4 hi = pack8_bf16(v);
         __builtin_nontemporal_store(hi, gv<u32x4>((uint16_t*)xout + off));
@@ -1050,7 +1053,7 @@ __device__ __forceinline__ DevMat load_stage_mat(const DevMat* src) {
   d.a = load_uniform(&src->a);
   d.mp = load_uniform(&src->mp);
   d.np = load_uniform(&src->np);
-  if (STAGE != 2) d.sc = load_uniform(&src->sc);
+  d.sc = load_uniform(&src->sc);
   if (STAGE >= 2) d.b = load_uniform(&src->b);
   if (STAGE == 3) {
     d.xlo = load_uniform(&src->xlo);
