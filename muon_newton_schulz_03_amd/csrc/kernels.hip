@@ -10,11 +10,15 @@
 //   momentum_kernel    M <- mu M + G (one fp32 rounding), U = G + mu M or M,
 //                      per-tile partial sums of U^2, X0 = U written in the
 //                      canonical (short side first) orientation.
-//   norm_kernel        s = 1 / (||U||_F + eps) per matrix.
-//   ns_stage_kernel<1> A = s^2 X X^T     (upper tiles; A stored upper-triangle only)
-//   ns_stage_kernel<2> B = b A + c A A    (A symmetric: A A = A A^T; B upper only)
-//   ns_stage_kernel<3> X <- a X + B X; on the last step W <- W - lr s O
-//   apply_kernel       T == 0: W <- W - lr s X0
+//   norm_kernel        s = 1 / (||U||_F + eps) per matrix; the first iteration's
+//                      X is s U, with U as stored.
+//   ns_stage_kernel<1> A = X X^T (upper tiles; A stored upper-triangle only);
+//                      s^2 U U^T in the first iteration
+//   ns_stage_kernel<2> B = b A + c A A (A symmetric: A A = A A^T; B upper only);
+//                      stored as s B in the first iteration (s folded into b, c)
+//   ns_stage_kernel<3> X <- a X + B X (first iteration: a s U + (s B) U); on
+//                      the last iteration W <- W - lr scale O
+//   apply_kernel       T == 0: W <- W - lr scale s U
 //
 // The three products share one MFMA main loop: 128x128 output tile per
 // 256-thread block (2 per CU), 4 waves each owning 64x64 as 2x2
