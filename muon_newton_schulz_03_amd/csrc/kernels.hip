@@ -963,8 +963,10 @@ __device__ __forceinline__ void tile_epilogue(const StageArgs& args, const DevMa
           }
         }
         if (STAGE == 1) {
+          if (t == 1) {  // uniform: later iterations skip the multiply
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] *= pre;
+            for (int e = 0; e < 8; ++e) v[e] *= pre;
+          }
         } else {
           float av[8];
           in_dir(q, av);
