@@ -176,6 +176,9 @@ __device__ __forceinline__ float block_inv_norm(const DevMat& d, double* scratch
 // consecutive columns of rows ty and ty + 32 of the ORIGINAL tile, so gradient
 // and momentum accesses are 16/32-byte vectors along the original rows; all
 // loads are issued before any store (stores share the in-order counter).
+// G and M are read once and M written once per step, with nontemporal
+// accesses, while X0 is stored normally: the first Gram launch reads it right
+// after, and it then stays in the caches more often.
 struct MomRow {
   float g[8], m[8];
   bool ok[8];
@@ -188,15 +191,17 @@ __device__ __forceinline__ void mom_load(const DevMat& d, int r, int c, MomRow& 
   x.vec = rowok && d.vec_g && c + 7 < d.cols;
   if (x.vec) {
     if (d.g_bf16) {
-      const u32x4 g8 = *gv<u32x4>((const uint16_t*)d.g + off);
+      const u32x4 g8 = __builtin_nontemporal_load(gv<u32x4>((const uint16_t*)d.g + off));
       unpack4_bf16(u32x2{g8.x, g8.y}, x.g);
       unpack4_bf16(u32x2{g8.z, g8.w}, x.g + 4);
     } else {
-      const f32x4 g0 = *gv<f32x4>((const float*)d.g + off), g1 = *gv<f32x4>((const float*)d.g + off + 4);
+      const f32x4 g0 = __builtin_nontemporal_load(gv<f32x4>((const float*)d.g + off));
+      const f32x4 g1 = __builtin_nontemporal_load(gv<f32x4>((const float*)d.g + off + 4));
       x.g[0] = g0.x; x.g[1] = g0.y; x.g[2] = g0.z; x.g[3] = g0.w;
       x.g[4] = g1.x; x.g[5] = g1.y; x.g[6] = g1.z; x.g[7] = g1.w;
     }
-    const f32x4 m0 = *gv<f32x4>(d.mom + off), m1 = *gv<f32x4>(d.mom + off + 4);
+    const f32x4 m0 = __builtin_nontemporal_load(gv<f32x4>(d.mom + off));
+    const f32x4 m1 = __builtin_nontemporal_load(gv<f32x4>(d.mom + off + 4));
     x.m[0] = m0.x; x.m[1] = m0.y; x.m[2] = m0.z; x.m[3] = m0.w;
     x.m[4] = m1.x; x.m[5] = m1.y; x.m[6] = m1.z; x.m[7] = m1.w;
 #pragma unroll
@@ -267,8 +272,8 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(MomArgs args) {
     const int r = r0 + ty + 32 * q, c = c0 + 8 * tx;
     const size_t off = (size_t)r * d.cols + c;
     if (x[q].vec) {
-      *gv<f32x4>(d.mom + off) = f32x4{mn[q][0], mn[q][1], mn[q][2], mn[q][3]};
-      *gv<f32x4>(d.mom + off + 4) = f32x4{mn[q][4], mn[q][5], mn[q][6], mn[q][7]};
+      __builtin_nontemporal_store(f32x4{mn[q][0], mn[q][1], mn[q][2], mn[q][3]}, gv<f32x4>(d.mom + off));
+      __builtin_nontemporal_store(f32x4{mn[q][4], mn[q][5], mn[q][6], mn[q][7]}, gv<f32x4>(d.mom + off + 4));
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
