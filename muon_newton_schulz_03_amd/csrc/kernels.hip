@@ -177,8 +177,9 @@ __device__ __forceinline__ float block_inv_norm(const DevMat& d, double* scratch
 // and momentum accesses are 16/32-byte vectors along the original rows; all
 // loads are issued before any store (stores share the in-order counter).
 // G and M are read once and M written once per step, with nontemporal
-// accesses, while X0 is stored normally: the first Gram launch reads it right
-// after, and it then stays in the caches more often.
+// accesses, and so are X0's low bytes (only the first update epilogue reads
+// them), while X0's bf16 copy is stored normally: the first Gram launch reads
+// it right after, and it then stays in the caches more often.
 struct MomRow {
   float g[8], m[8];
   bool ok[8];
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(MomArgs args) {
       const u32x2 h0 = pack4_bf16(xv[q][0], xv[q][1], xv[q][2], xv[q][3]);
       const u32x2 h1 = pack4_bf16(xv[q][4], xv[q][5], xv[q][6], xv[q][7]);
       *gv<u32x4>((uint16_t*)d.xo[0] + xo) = u32x4{h0.x, h0.y, h1.x, h1.y};
-      if (d.xlo) *gv<u32x2>(d.xlo + xo) = u32x2{pack4_lo(xv[q], h0), pack4_lo(xv[q] + 4, h1)};
+      if (d.xlo) __builtin_nontemporal_store(u32x2{pack4_lo(xv[q], h0), pack4_lo(xv[q] + 4, h1)}, gv<u32x2>(d.xlo + xo));
     }
   }
 
