@@ -175,7 +175,7 @@ const char* muon_last_error(void);
 typedef struct muon_plan_info {
   int64_t workspace_bytes;
   int32_t n_matrices;
-  int32_t tile;              /* tile edge of the Newton-Schulz products */
+  int32_t tile;              /* tile edge of the fp32 Newton-Schulz products (128) */
   int32_t blocks[MUON_KIND_COUNT]; /* tile-table length of each launch kind: the grid of
                                       the momentum, norm and apply launches; the product
                                       kernels are persistent (2 blocks per CU) and
@@ -190,6 +190,9 @@ typedef struct muon_plan_info {
                                 4): momentum and norm have n_groups launches per
                                 step, a product kind T * n_groups (times the
                                 precisions present) */
+  int32_t bf16_tile_rows;    /* bf16 products: output tile rows (256); the short side
+                                of such a matrix is padded to a multiple of it */
+  int32_t bf16_tile_cols;    /* bf16 products: output tile columns (128) */
 } muon_plan_info;
 
 int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts,

@@ -42,7 +42,8 @@ class Options(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [("workspace_bytes", ctypes.c_int64), ("n_matrices", ctypes.c_int32), ("tile", ctypes.c_int32),
                 ("blocks", ctypes.c_int32 * KIND_COUNT), ("x_master_iters", ctypes.c_int32),
-                ("path", ctypes.c_int32), ("n_f32_matrices", ctypes.c_int32), ("n_groups", ctypes.c_int32)]
+                ("path", ctypes.c_int32), ("n_f32_matrices", ctypes.c_int32), ("n_groups", ctypes.c_int32),
+                ("bf16_tile_rows", ctypes.c_int32), ("bf16_tile_cols", ctypes.c_int32)]
 
 
 class MuonError(RuntimeError):
@@ -54,16 +55,12 @@ class MuonError(RuntimeError):
 _lib = None
 
 
-def load(path: str = None) -> ctypes.CDLL:
-    """Load the built library (fails loudly if it has not been built).
-
-    ``MUON_LIBRARY`` in the environment selects another build of the same
-    library (for comparing build variants); the default is the in-tree build.
-    """
+def load() -> ctypes.CDLL:
+    """Load the in-tree build of the library (fails loudly if it has not been built)."""
     global _lib
     if _lib is not None:
         return _lib
-    path = path or os.environ.get("MUON_LIBRARY") or LIB_PATH
+    path = LIB_PATH
     if not os.path.exists(path):
         raise FileNotFoundError(f"{path} is missing: build it with `python -m muon_newton_schulz_03_amd.build`")
     lib = ctypes.CDLL(path)

@@ -20,6 +20,9 @@ hipError_t launch_apply(const ApplyArgs& args, int blocks, hipStream_t stream, h
 hipError_t launch_stage(int stage, bool f32, const StageArgs& args, int blocks, hipStream_t stream, hipEvent_t ev0,
                         hipEvent_t ev1);
 hipError_t prepare_stage_kernels();
+hipError_t launch_stage_bf16(int stage, const StageArgs& args, int blocks, hipStream_t stream, hipEvent_t ev0,
+                             hipEvent_t ev1);
+hipError_t prepare_bf16_kernels();
 hipError_t launch_norm(const DevMat* mats, int n, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 }  // namespace muon
 
@@ -103,6 +106,11 @@ int check_desc(const muon_matrix_desc& d, int idx, bool need_ptrs) {
     return fail(MUON_E_UNSUPPORTED, "matrix %d: w_dtype %d unsupported", idx, d.w_dtype);
   if (d.reserved != 0) return fail(MUON_E_INVAL, "matrix %d: reserved field must be 0", idx);
   if (!std::isfinite(d.scale)) return fail(MUON_E_INVAL, "matrix %d: scale is not finite", idx);
+  // the kernels address each matrix's buffers with 32-bit byte offsets
+  const int64_t mp = round_up(std::min(d.rows, d.cols), kTileRowsBf16), np = round_up(std::max(d.rows, d.cols), kTile);
+  if (mp * np * 4 >= (int64_t(1) << 31) || d.rows * d.cols * 4 >= (int64_t(1) << 31))
+    return fail(MUON_E_UNSUPPORTED, "matrix %d: %lld x %lld needs more than 2 GiB per buffer", idx,
+                (long long)d.rows, (long long)d.cols);
   if (need_ptrs) {
     if (!d.weight || !d.grad || !d.momentum) return fail(MUON_E_INVAL, "matrix %d: null device pointer", idx);
     if (d.weight == d.grad || d.weight == (void*)d.momentum || d.grad == (const void*)d.momentum)
@@ -138,11 +146,13 @@ Geometry geometry(const muon_matrix_desc& d, int path) {
   g.tr = d.rows > d.cols;
   g.m = (int)std::min(d.rows, d.cols);
   g.n = (int)std::max(d.rows, d.cols);
-  g.mp = (int)round_up(g.m, kTile);
+  g.f32 = path == MUON_PATH_F32 || g.m < kMinBf16Side;
+  // bf16 products run 256 x 128 tiles (rows of X, A, B in 256-row panels),
+  // fp32 products 128 x 128 tiles
+  g.mp = (int)round_up(g.m, g.f32 ? kTile : kTileRowsBf16);
   g.np = (int)round_up(g.n, kTile);
   g.mom_n = g.np / kMomTile;
   g.nparts = (g.mp / kMomTile) * g.mom_n;
-  g.f32 = path == MUON_PATH_F32 || g.m < kMinBf16Side;
   return g;
 }
 
@@ -172,28 +182,34 @@ constexpr int kProductGrid = kXcds * kBlocksPerXcd;
 // would reach if each took the next tile when it finished.  Block j of XCD x
 // (block index 8j + x) finds its r-th tile at entry 8(r * kBlocksPerXcd + j) + x;
 // entries of blocks with fewer tiles hold null tiles that exit at once.
-std::vector<Tile> xcd_order(const std::vector<std::vector<Tile>>& per_mat, const std::vector<double>& tile_cost) {
+struct CostTile {
+  Tile t;
+  double cost;  // work of this tile (128 x 128 x 128 units)
+};
+std::vector<Tile> xcd_order(const std::vector<std::vector<CostTile>>& per_mat, const std::vector<double>& tile_cost) {
   const int nm = (int)per_mat.size();
   std::vector<int> order(nm);
   for (int i = 0; i < nm; ++i) order[i] = i;
   std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return tile_cost[x] > tile_cost[y]; });
-  std::vector<std::vector<Tile>> runs(kXcds);
+  std::vector<std::vector<CostTile>> runs(kXcds);
   // one cost class (matrices whose tiles cost the same) at a time, so that
   // every XCD gets its share of long and of short tiles
   for (size_t c0 = 0; c0 < order.size();) {
     size_t c1 = c0;
     double total = 0.0;
-    while (c1 < order.size() && tile_cost[order[c1]] == tile_cost[order[c0]])
-      total += tile_cost[order[c1]] * per_mat[order[c1]].size(), ++c1;
+    while (c1 < order.size() && tile_cost[order[c1]] == tile_cost[order[c0]]) {
+      for (const CostTile& t : per_mat[order[c1]]) total += t.cost;
+      ++c1;
+    }
     double acc = 0.0;
     for (size_t q = c0; q < c1 && total > 0.0; ++q) {
       const int i = order[q];
-      for (const Tile& t : per_mat[i]) {
+      for (const CostTile& t : per_mat[i]) {
         // the run whose cost share contains the midpoint of this tile
-        int x = (int)((acc + 0.5 * tile_cost[i]) * kXcds / total);
+        int x = (int)((acc + 0.5 * t.cost) * kXcds / total);
         x = std::min(std::max(x, 0), kXcds - 1);
         runs[x].push_back(t);
-        acc += tile_cost[i];
+        acc += t.cost;
       }
     }
     c0 = c1;
@@ -203,11 +219,11 @@ std::vector<Tile> xcd_order(const std::vector<std::vector<Tile>>& per_mat, const
   size_t rounds = 0;
   for (int x = 0; x < kXcds; ++x) {
     std::vector<double> load(kBlocksPerXcd, 0.0);
-    for (const Tile& t : runs[x]) {
+    for (const CostTile& t : runs[x]) {
       const int j = (int)(std::min_element(load.begin(), load.end()) - load.begin());
-      load[j] += tile_cost[t.mat];
+      load[j] += t.cost;
       std::vector<Tile>& l = blk[(size_t)x * kBlocksPerXcd + j];
-      l.push_back(t);
+      l.push_back(t.t);
       rounds = std::max(rounds, l.size());
     }
   }
@@ -256,25 +272,45 @@ Tables build_tables(const std::vector<Geometry>& geo, int groups) {
   };
   for (int grp = 0; grp < kGroups; ++grp)
   for (int prec = 0; prec < 2; ++prec) {
-    std::vector<std::vector<Tile>> sym(nm), upd(nm);
-    std::vector<double> gram_cost(nm), poly_cost(nm), upd_cost(nm);
+    std::vector<std::vector<CostTile>> gram(nm), poly(nm), upd(nm);
+    std::vector<double> gram_k(nm), poly_k(nm), upd_k(nm);  // cost classes: K of the tiles
     for (int i = 0; i < nm; ++i) {
       const Geometry& g = geo[i];
       if (g.f32 != prec || group_of(i) != grp) continue;
-      const int tm = g.mp / kTile, tn = g.np / kTile;
-      for (int a = 0; a < tm; ++a)
-        for (int b = a; b < tm; ++b) sym[i].push_back(Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0});
-      // update tiles column by column: the tm tiles of one X column panel run
-      // together and share it in L2
-      for (int b = 0; b < tn; ++b)
-        for (int a = 0; a < tm; ++a) upd[i].push_back(Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0});
-      gram_cost[i] = (double)g.np;  // K of each product tile
-      poly_cost[i] = (double)g.mp;
-      upd_cost[i] = (double)g.mp;
+      const double K1 = g.np / 128.0, K2 = g.mp / 128.0;
+      if (prec == 0) {
+        // bf16: 256 x 128 tiles (row panel a of 256 rows, column panel b of 128);
+        // symmetric products take the tiles reaching the upper triangle at 128
+        // granularity; when b == 2a, rows 128..255 lie below it (half the work)
+        const int tm = g.mp / kTileRowsBf16, tc = g.mp / kTile, tn = g.np / kTile;
+        for (int a = 0; a < tm; ++a)
+          for (int b = 2 * a; b < tc; ++b) {
+            const double halves = b == 2 * a ? 1.0 : 2.0;
+            gram[i].push_back(CostTile{Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0}, halves * K1});
+            poly[i].push_back(CostTile{Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0}, halves * K2});
+          }
+        // update tiles column panel by column panel: the tiles of one X column
+        // panel run together and share it in L2
+        for (int b = 0; b < tn; ++b)
+          for (int a = 0; a < tm; ++a) upd[i].push_back(CostTile{Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0}, 2.0 * K2});
+      } else {
+        // fp32: 128 x 128 tiles, upper triangle of the symmetric products
+        const int tm = g.mp / kTile, tn = g.np / kTile;
+        for (int a = 0; a < tm; ++a)
+          for (int b = a; b < tm; ++b) {
+            gram[i].push_back(CostTile{Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0}, K1});
+            poly[i].push_back(CostTile{Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0}, K2});
+          }
+        for (int b = 0; b < tn; ++b)
+          for (int a = 0; a < tm; ++a) upd[i].push_back(CostTile{Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0}, K2});
+      }
+      gram_k[i] = K1;
+      poly_k[i] = K2;
+      upd_k[i] = K2;
     }
-    t.ns[grp][prec][kGram] = xcd_order(sym, gram_cost);
-    t.ns[grp][prec][kPoly] = xcd_order(sym, poly_cost);
-    t.ns[grp][prec][kUpd] = xcd_order(upd, upd_cost);
+    t.ns[grp][prec][kGram] = xcd_order(gram, gram_k);
+    t.ns[grp][prec][kPoly] = xcd_order(poly, poly_k);
+    t.ns[grp][prec][kUpd] = xcd_order(upd, upd_k);
   }
   for (int i = 0; i < nm; ++i) {
     const Geometry& g = geo[i];
@@ -513,7 +549,11 @@ int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts
     info->workspace_bytes = (int64_t)total;
     info->n_matrices = n;
     info->tile = kTile;
-    info->blocks[MUON_KIND_MOMENTUM] = (int32_t)(t.mom[0].size() + t.mom[1].size());
+    info->bf16_tile_rows = kTileRowsBf16;
+    info->bf16_tile_cols = kTile;
+    size_t nmom = 0;
+    for (int grp = 0; grp < kGroups; ++grp) nmom += t.mom[grp].size();
+    info->blocks[MUON_KIND_MOMENTUM] = (int32_t)nmom;
     info->blocks[MUON_KIND_GRAM] = (int32_t)concat_tables(t, kGram).size();
     info->blocks[MUON_KIND_POLY] = (int32_t)concat_tables(t, kPoly).size();
     info->blocks[MUON_KIND_UPDATE] = (int32_t)concat_tables(t, kUpd).size();
@@ -533,8 +573,7 @@ int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts
     switch (kind) {
       case MUON_KIND_MOMENTUM:
       case MUON_KIND_APPLY:
-        v = t.mom[0];
-        v.insert(v.end(), t.mom[1].begin(), t.mom[1].end());
+        for (int grp = 0; grp < kGroups; ++grp) v.insert(v.end(), t.mom[grp].begin(), t.mom[grp].end());
         break;
       case MUON_KIND_GRAM:
       case MUON_KIND_POLY:
@@ -610,6 +649,7 @@ int muon_init(const muon_matrix_desc* descs, int n, const muon_options* opts, vo
     if (e != hipSuccess) return cleanup(hip_fail(e, "hipEventCreate"));
   }
   e = prepare_stage_kernels();
+  if (e == hipSuccess) e = prepare_bf16_kernels();
   if (e != hipSuccess) return cleanup(hip_fail(e, "hipFuncSetAttribute(dynamic LDS)"));
 
   // Tile tables: staged through pinned memory, uploaded once; init waits for
@@ -760,7 +800,9 @@ static int step_impl(muon_plan* p, const muon_matrix_desc* descs, int n, const f
       // table is shorter (a multiple of 8: every block keeps its XCD)
       const int grid = std::min((ntab + 7) / 8 * 8, kProductGrid);
       if ((rc = prof_events(p, kKinds[k], &ev))) return rc;
-      if ((rc = check_launch(launch_stage(k + 1, prec == 1, sa, grid, s, ev.start, ev.stop), kNames[k]))) return rc;
+      const hipError_t le = prec == 1 ? launch_stage(k + 1, true, sa, grid, s, ev.start, ev.stop)
+                                      : launch_stage_bf16(k + 1, sa, grid, s, ev.start, ev.stop);
+      if ((rc = check_launch(le, kNames[k]))) return rc;
     }
     return MUON_OK;
   };

@@ -13,7 +13,8 @@
 
 namespace muon {
 
-constexpr int kTile = 128;     // NS product tile edge (rows and columns)
+constexpr int kTile = 128;     // NS product tile edge (fp32 products; columns of bf16 tiles)
+constexpr int kTileRowsBf16 = 256;  // rows of a bf16 product tile (X, A, B padded to multiples of it)
 constexpr int kMomTile = 64;   // momentum kernel tile edge
 constexpr int kThreads = 256;  // threads per block, every kernel
 constexpr int kXcds = 8;       // MI355X: 8 XCDs, blocks dispatched round-robin

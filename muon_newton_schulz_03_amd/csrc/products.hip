@@ -1,0 +1,796 @@
+// gfx950 (CDNA4) bf16 Newton-Schulz products of the Muon step on 256x128 tiles.
+//
+// The iteration (overview page "The NanoGPT speedrun", paragraph "Six records
+// account for most of the speedup", record #3: the update is driven towards
+// its polar factor by Newton-Schulz steps):
+//   stage 1  A = X X^T             (K = n)
+//   stage 2  B = b A + c A A       (K = m; A is symmetric, so A A = A A^T)
+//   stage 3  X <- a X + B X        (K = m); the last iteration applies the
+//            weight step W <- W - lr scale O instead of storing X
+//
+// Design (one persistent kernel per product kind):
+//   * output tile 256 rows x 128 columns per 256-thread block, two blocks per
+//     CU; wave w owns rows 128 (w >> 1) .. +127 and columns 64 (w & 1) .. +63
+//     as 4 x 2 v_mfma_f32_32x32x16_bf16 blocks (128 accumulator registers).
+//     Per K step a wave reads 4 + 2 fragments from LDS for 8 MFMAs (64x64
+//     wave tiles read twice as many per MFMA), and a block moves 48 bytes
+//     from L2 per 512 FLOP-clocks of its CU (64 for 128x128 tiles);
+//   * X, its low bytes, A and B are stored in 128-row x 32-column tiles (each
+//     tile contiguous), so a K slab of 32 elements of a 128-row panel is one
+//     contiguous 8 KiB tile: every direct-to-LDS request reads 1 KiB of
+//     contiguous memory (whole cache lines), and every 32 x 32 output block
+//     is 2 KiB of contiguous memory;
+//   * K streams in 32-element slabs through a three-slot LDS ring filled by
+//     direct-to-LDS buffer loads; slab kt + 2 is requested as slab kt
+//     starts, and the ring runs on from one tile into the next, so a tile's
+//     first two slabs are in flight during the previous tile's epilogue;
+//   * A and B are stored in full.  Stages 1 and 2 compute only tiles that
+//     reach the upper triangle (at 128 granularity) and write every element
+//     at (i, j) and at (j, i); diagonal 32-blocks are made exactly symmetric
+//     first.  So every operand is read K-contiguous (ds_read_b128), except X
+//     as the right operand of B X, read with the transposing
+//     ds_read_b64_tr_b16;
+//   * stage 3 adds a X inside the K loop: the X slab of K rows k0 .. k0 + 31
+//     holds X at exactly the output rows k0 .. k0 + 31 of the tile's columns,
+//     so the wave owning those rows reads them there (with X's low bytes,
+//     copied into LDS beside the ring for those slabs) and adds a x to its
+//     accumulators; the epilogue then only stores;
+//   * the epilogue stages one 32 x 32 accumulator block at a time in LDS, per
+//     wave and without block barriers, so that global accesses run along
+//     rows; the inputs it still needs (A in stage 2, W in the weight step) are
+//     requested blocks ahead, and the next tile's first waits allow for the
+//     epilogue's stores still in flight.
+#include "device_common.h"
+
+namespace muon {
+namespace {
+
+constexpr int kTM = 256;                      // tile rows (Q operand's panel)
+constexpr int kTN = 128;                      // tile columns (P operand's panel)
+constexpr int kBK = 32;                       // K elements per slab
+constexpr int kHalf = 128 * 2 * kBK;          // one 128-row half slab: 8 KiB
+constexpr int kSlot = 3 * kHalf;              // Q rows 0..127, Q rows 128..255, P
+constexpr int kRing = 3;
+constexpr int kLoBuf = kBK * kTN;             // X's low bytes of one slab: 4 KiB
+constexpr int kLoBase = kRing * kSlot;        // two low-byte buffers after the ring
+constexpr int kLds = kLoBase + 2 * kLoBuf;    // 80 KiB: two blocks per CU
+constexpr int kBlock = 32 * 32 * 4;           // one staged 32 x 32 fp32 block per wave
+constexpr int kBlocks = 2;                    // resident blocks per CU
+constexpr uint32_t kOob = 0x80000000u;        // buffer offset past every resource: load 0, store dropped
+constexpr int kDma = 6;                       // ring requests per wave per slab
+
+// Swizzles (16-byte chunk c of row r sits at chunk c ^ swz(r)), each checked
+// in a bank model of 16 lanes per 256-byte cycle for its access patterns.
+// K-contiguous half slab (64-byte rows): MFMA fragment reads (32 rows x one
+// chunk per 32 lanes) conflict-free.
+__device__ __forceinline__ int kc_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+// X slab of B X (32 K rows x 128 columns, four 32-column tiles; in LDS as
+// [tile][32 rows][64 bytes]): transposing fragment reads (4 K rows x 2 chunks
+// per 16 lanes) and row reads of the a X term (16 rows x one chunk)
+// conflict-free.
+__device__ __forceinline__ int xs_swz(int k) { return (k >> 2) & 3; }
+// Low bytes of that slab ([tile][32 rows][32 bytes], 16-byte halves of row k
+// at half ^ lo_swz(k)): row reads conflict-free.
+__device__ __forceinline__ int lo_swz(int k) { return (k >> 3) & 1; }
+// Staged 32 x 32 fp32 block (128-byte rows): accumulator writes and row passes
+// conflict-free, 4 x 4 block reads 2-way.
+__device__ __forceinline__ int st_swz(int r) { return (r >> 1) & 7; }
+
+// Two of the eight 1 KiB instructions that fill a K-contiguous half slab
+// from one contiguous 8 KiB tile (128 rows x 64 bytes): instruction n moves
+// rows 16 n .. 16 n + 15, lane l row 16 n + l / 4 at physical chunk l % 4,
+// i.e. logical chunk (l % 4) ^ kc_swz(row).
+__device__ __forceinline__ void dma_half(char* lds, rsrc_t rs, uint32_t tile, int w, int lane) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int n = 2 * w + q;
+    const int row = 16 * n + (lane >> 2);
+    const uint32_t voff = tile + (uint32_t)row * 64u + 16u * (uint32_t)((lane & 3) ^ kc_swz(row));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MUON_LDS(lds + n * 1024), 16, voff, 0, 0, 0);
+  }
+}
+// Two of the eight instructions that copy the X slab of B X: 32 K rows of
+// four consecutive 32-column tiles, 2 KiB contiguous in each (`piece` is the
+// first one's byte offset, the next ones follow 8 KiB apart); instruction n
+// moves rows 16 (n % 2) .. +15 of tile n / 2.
+__device__ __forceinline__ void dma_xslab(char* lds, rsrc_t rs, uint32_t piece, int w, int lane) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int n = 2 * w + q;
+    const int k = 16 * (n & 1) + (lane >> 2);
+    const uint32_t voff = piece + (uint32_t)(n >> 1) * 8192u + (uint32_t)k * 64u +
+                          16u * (uint32_t)((lane & 3) ^ xs_swz(k));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MUON_LDS(lds + n * 1024), 16, voff, 0, 0, 0);
+  }
+}
+// One of the four instructions that copy the X slab's low bytes (32 rows x 32
+// bytes of four consecutive tiles, 1 KiB contiguous in each, 4 KiB apart):
+// wave w moves tile w's rows.
+__device__ __forceinline__ void dma_lo(char* lds, rsrc_t rs, uint32_t piece, int w, int lane) {
+  const int k = lane >> 1;
+  const uint32_t voff = piece + (uint32_t)w * 4096u + (uint32_t)k * 32u + 16u * (uint32_t)((lane & 1) ^ lo_swz(k));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MUON_LDS(lds + w * 1024), 16, voff, 0, 0, 0);
+}
+
+// Two transposing-read fragments of the X slab (columns base + 0..31 and
+// base + 32..63, K step ks): in a 16-lane group, lane r addresses K row
+// k0 + r / 4, columns J0 + 4 (r % 4) .. +3, and lane i receives K rows
+// k0 .. k0 + 3 of column J0 + i, the MFMA operand layout.  The reads and their
+// wait sit in one asm block: the compiler would otherwise wait for every
+// in-flight direct-to-LDS load first.
+__device__ __forceinline__ void frags_xs(u32x4 (&f)[2], const char* l, int base, int lane, int ks) {
+  const int g = lane >> 4, r = lane & 15;
+  uint32_t addr[2][2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int jel = base + n * 32 + 16 * (g & 1) + 4 * (r & 3);  // first of 4 columns
+    const int tile = jel >> 5, chunk = (jel & 31) >> 3, half = (jel >> 2) & 1;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int k = 16 * ks + 8 * (g >> 1) + 4 * m + (r >> 2);
+      addr[n][m] = (uint32_t)(uintptr_t)(l + tile * 2048 + k * 64 + ((chunk ^ xs_swz(k)) << 4) + (half << 3));
+    }
+  }
+  u32x2 t00, t01, t10, t11;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(t00), "=&v"(t01), "=&v"(t10), "=&v"(t11)
+      : "v"(addr[0][0]), "v"(addr[0][1]), "v"(addr[1][0]), "v"(addr[1][1])
+      : "memory");
+  f[0] = u32x4{t00.x, t00.y, t01.x, t01.y};
+  f[1] = u32x4{t10.x, t10.y, t11.x, t11.y};
+}
+
+// Where one tile's operands are (byte offsets into the tiled matrices).
+struct Ctx {
+  const void* q;            // row-panel source (X, A or B)
+  const void* p;            // column-panel source (X or A); null: empty requests
+  const uint8_t* xlo;       // stage 3 with the low bytes: X's low bytes
+  uint32_t qbytes, pbytes;  // sizes of the two matrices
+  uint32_t qoff;            // tile (row block of Q's rows 0..127, K slab 0)
+  uint32_t qblk;            // bytes per 128-row block of Q's matrix
+  uint32_t poff;            // stages 1, 2: tile (P's row block, K slab 0); stage 3: X tile (0, 4 tj)
+  uint32_t pblk;            // bytes per 128-row block of P's matrix
+  int nk;                   // K slabs
+  int i0, j0;               // output origin
+  int psrc;                 // 0: P from its own slab region; 1, 2: from Q half 0, 1
+  int skip1;                // rows 128..255 of the tile have nothing to compute
+};
+
+template <int STAGE, int MODE>
+__device__ __forceinline__ Ctx ctx_of(const StageArgs& args, const Tile& tl) {
+  const DevMat* m = args.mats + tl.mat;
+  const uint32_t mp = (uint32_t)load_uniform(&m->mp), np = (uint32_t)load_uniform(&m->np);
+  const void* xin = ((args.t - 1) & 1) ? load_uniform(&m->xo[1]) : load_uniform(&m->xo[0]);
+  Ctx c;
+  c.i0 = tl.ti * kTM;
+  c.j0 = tl.tj * kTN;
+  c.psrc = 0;
+  c.skip1 = 0;
+  c.xlo = nullptr;
+  const uint32_t xb = mp * np * 2u, ab = mp * mp * 2u;
+  if (STAGE == 1 || STAGE == 2) {
+    const uint32_t K = STAGE == 1 ? np : mp;
+    c.q = c.p = STAGE == 1 ? xin : (const void*)load_uniform(&m->a);
+    c.qbytes = c.pbytes = STAGE == 1 ? xb : ab;
+    c.qblk = c.pblk = K * 256u;  // (K / 32) tiles of 8 KiB
+    c.qoff = (uint32_t)(c.i0 >> 7) * c.qblk;
+    c.poff = (uint32_t)(c.j0 >> 7) * c.pblk;
+    c.nk = (int)K / kBK;
+    // the column panel is one of the row halves on the tile's diagonal
+    const int rel = tl.tj - 2 * tl.ti;
+    if (rel == 0 || rel == 1) c.psrc = rel + 1;
+    c.skip1 = rel == 0;  // rows 128..255 lie below the diagonal
+  } else {
+    c.q = load_uniform(&m->b);
+    c.qbytes = ab;
+    c.qblk = mp * 256u;
+    c.qoff = (uint32_t)(c.i0 >> 7) * c.qblk;
+    c.p = xin;
+    c.pbytes = xb;
+    c.pblk = np * 256u;
+    c.poff = (uint32_t)(c.j0 >> 5) * 8192u;
+    c.nk = (int)mp / kBK;
+    if (MODE & kHiLo) c.xlo = load_uniform(&m->xlo);
+  }
+  return c;
+}
+
+// Request slab kt of a tile into ring slot `slot` (kDma instructions per wave;
+// parts the tile does not need get empty resources, which move nothing).
+template <int STAGE>
+__device__ __forceinline__ void issue_slab(char* smem, const Ctx& c, int kt, int slot, int w, int lane) {
+  char* s = smem + slot * kSlot;
+  const uint32_t kb = (uint32_t)kt * 8192u;
+  dma_half(s, make_rsrc(c.q, c.p ? c.qbytes : 0u), c.qoff + kb, w, lane);
+  dma_half(s + kHalf, make_rsrc(c.q, c.p && !c.skip1 ? c.qbytes : 0u), c.qoff + c.qblk + kb, w, lane);
+  const rsrc_t p = make_rsrc(c.p, c.p && !c.psrc ? c.pbytes : 0u);
+  if (STAGE == 3)
+    dma_xslab(s + 2 * kHalf, p, c.poff + (uint32_t)(kt >> 2) * c.pblk + (uint32_t)(kt & 3) * 2048u, w, lane);
+  else
+    dma_half(s + 2 * kHalf, p, c.poff + kb, w, lane);
+}
+
+// Request X's low bytes of slab kt into low-byte buffer `buf` (1 instruction
+// per wave; empty unless the slab's K rows are output rows of the tile).
+__device__ __forceinline__ void issue_lo(char* smem, const Ctx& c, int kt, int buf, int w, int lane) {
+  const bool need = c.p && kt * kBK >= c.i0 && kt * kBK < c.i0 + kTM;
+  dma_lo(smem + kLoBase + buf * kLoBuf, make_rsrc(c.xlo, need ? (c.pbytes >> 1) : 0u),
+         (c.poff >> 1) + (uint32_t)(kt >> 2) * (c.pblk >> 1) + (uint32_t)(kt & 3) * 1024u, w, lane);
+}
+
+// Per-lane byte offsets of the K-contiguous fragment reads: lane l reads row
+// 32 m + l % 32 of a half at logical chunk 2 ks + l / 32.
+struct FragOff {
+  uint32_t row, ch[2];
+};
+__device__ __forceinline__ FragOff frag_off(int lane) {
+  FragOff f;
+  const int r = lane & 31, sw = kc_swz(r);
+  f.row = (uint32_t)r * 64u;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) f.ch[ks] = (uint32_t)(((2 * ks + (lane >> 5)) ^ sw) << 4);
+  return f;
+}
+
+// One slab: acc[mi][nj] += P(columns) x Q(rows)^T over 32 K.  MFMA operand A
+// is the P fragment (MFMA row <-> output column), operand B the Q fragment,
+// so lane l holds output row 32 mi + l % 32 and 4 consecutive output columns
+// per group of 4 accumulator registers.
+template <bool PX>
+__device__ __forceinline__ void mma_slab(f32x16 (&acc)[4][2], const char* qh, const char* p, int wn, int lane,
+                                         const FragOff& fo) {
+  u32x4 qf[2][4], pf[2][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) qf[ks][mi] = *(const u32x4*)(qh + mi * 2048 + fo.row + fo.ch[ks]);
+    if (PX) {
+      frags_xs(pf[ks], p, 64 * wn, lane, ks);
+    } else {
+#pragma unroll
+      for (int nj = 0; nj < 2; ++nj) pf[ks][nj] = *(const u32x4*)(p + (2 * wn + nj) * 2048 + fo.row + fo.ch[ks]);
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < 2; ++nj)
+        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pf[ks][nj]),
+                                                               __builtin_bit_cast(bf16x8, qf[ks][mi]), acc[mi][nj],
+                                                               0, 0, 0);
+}
+
+// Stage 3: acc block row mi += alpha x, x = X at the output rows that the X
+// slab in LDS holds (K row l % 32 of the slab is output row 32 mi + l % 32 of
+// the wave), decoded with its low bytes when LO.
+template <bool LO>
+__device__ __forceinline__ void fold_x(f32x16 (&a)[2], const char* p, const char* lo, int wn, int lane, float alpha) {
+  const int k = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int nj = 0; nj < 2; ++nj)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int tile = 2 * wn + nj;  // the 32-column tile of these 4 columns
+      const u32x2 hi = *(const u32x2*)(p + tile * 2048 + k * 64 + ((g ^ xs_swz(k)) << 4) + 8 * h);
+      float x[4];
+      if (LO) {
+        const uint32_t lw =
+            *(const uint32_t*)(lo + tile * 1024 + k * 32 + (((g >> 1) ^ lo_swz(k)) << 4) + 8 * (g & 1) + 4 * h);
+        unpack4_hilo(hi, lw, x);
+      } else {
+        unpack4_bf16(hi, x);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[nj][4 * g + e] = fmaf(alpha, x[e], a[nj][4 * g + e]);
+    }
+}
+
+// ------------------------------------------------------------- epilogue --
+
+// The wave's staged 32 x 32 fp32 block (128-byte rows).
+struct Stage {
+  char* base;
+  __device__ __forceinline__ f32x4* at(int r, int cc) const {
+    return (f32x4*)(base + r * 128 + ((cc ^ st_swz(r)) << 4));
+  }
+  __device__ __forceinline__ float* elem(int r, int col) const {
+    return (float*)(base + r * 128 + (((col >> 2) ^ st_swz(r)) << 4)) + (col & 3);
+  }
+  // accumulator block: lane l holds row l % 32, columns 8 g + 4 (l / 32) .. +3
+  __device__ __forceinline__ void put(const f32x16& a, int lane) const {
+    const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) *at(r, 2 * g + h) = f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+  }
+};
+
+// Row pass p (0, 1): lane l handles row 16 p + l / 4, columns 8 (l % 4) .. +7.
+__device__ __forceinline__ int rp_row(int p, int lane) { return 16 * p + (lane >> 2); }
+__device__ __forceinline__ int rp_col(int lane) { return 8 * (lane & 3); }
+// Block pass: lane l handles the 4 x 4 block at rows 4 (l % 8) .., columns 4 (l / 8) ..
+__device__ __forceinline__ int bp_row(int lane) { return 4 * (lane & 7); }
+__device__ __forceinline__ int bp_col(int lane) { return 4 * (lane >> 3); }
+
+__device__ __forceinline__ void read8(const Stage& st, int r, int c, float* v) {
+  const f32x4 x = *st.at(r, c >> 2), y = *st.at(r, (c >> 2) + 1);
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+}
+__device__ __forceinline__ void write8(const Stage& st, int r, int c, const float* v) {
+  *st.at(r, c >> 2) = f32x4{v[0], v[1], v[2], v[3]};
+  *st.at(r, (c >> 2) + 1) = f32x4{v[4], v[5], v[6], v[7]};
+}
+// blk[e][f] = block[r + e][c + f]
+__device__ __forceinline__ void read_block(const Stage& st, int r, int c, float (&blk)[4][4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const f32x4 x = *st.at(r + e, c >> 2);
+    blk[e][0] = x.x; blk[e][1] = x.y; blk[e][2] = x.z; blk[e][3] = x.w;
+  }
+}
+// A diagonal 32-block of A or B: strictly lower elements take the values of
+// their mirrors, so that the block is exactly symmetric (reads before writes).
+__device__ __forceinline__ void symmetrize(const Stage& st, int lane) {
+  const int r = lane & 31, c0 = 16 * (lane >> 5);
+  float v[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] = c0 + e < r ? *st.elem(c0 + e, r) : 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if (c0 + e < r) *st.elem(r, c0 + e) = v[e];
+}
+
+__device__ __forceinline__ void store_b128(rsrc_t rs, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), rs,
+                                         off, 0, 0);
+}
+__device__ __forceinline__ void store_b64(rsrc_t rs, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, v), rs,
+                                        off, 0, 0);
+}
+
+// Weight step (stage 3, last iteration), W element (R, C) of the caller's
+// row-major matrix.  The common case, fp32 W with rows of a multiple of 4
+// elements on 16-byte boundaries ("fast"), takes 16-byte accesses requested
+// blocks ahead, all issued (out-of-range lanes get an offset past the
+// resource) so that the instruction counts are static; any other W (bf16,
+// ragged rows) takes a compact element-by-element loop.
+struct WRes {
+  rsrc_t r;
+  int rows, cols, bf16, fast;
+  float lr;
+};
+__device__ __forceinline__ uint32_t woff(const WRes& w, int R, int C) {
+  return R < w.rows && C < w.cols ? ((uint32_t)R * (uint32_t)w.cols + (uint32_t)C) << 2 : kOob;
+}
+__device__ __forceinline__ u32x4 wload4(const WRes& w, int R, int C) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.r, woff(w, R, C), 0, 0));
+}
+__device__ __forceinline__ void wstore4(const WRes& w, int R, int C, const float* v) {
+  store_b128(w.r, woff(w, R, C),
+             u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
+}
+// W (R, C) -= lr * o for one element of any W (bounds-checked, not unrolled)
+__device__ __forceinline__ void wstep1(const WRes& w, int R, int C, float o) {
+  if (R >= w.rows || C >= w.cols) return;
+  const uint32_t e = (uint32_t)R * (uint32_t)w.cols + (uint32_t)C;
+  if (w.bf16) {
+    const float x = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(w.r, e << 1, 0, 0) << 16);
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f2bf(fmaf(-w.lr, o, x)), w.r, e << 1, 0, 0);
+  } else {
+    const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(w.r, e << 2, 0, 0));
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(-w.lr, o, x)), w.r, e << 2, 0, 0);
+  }
+}
+
+// vmcnt(n), rounded down to the nearest supported immediate (waiting for more
+// than needed is always correct); n is wave-uniform.
+__device__ __forceinline__ void wait_vm(int n) {
+  if (n >= 62) MUON_WAIT_VMCNT(62);
+  else if (n >= 56) MUON_WAIT_VMCNT(56);
+  else if (n >= 48) MUON_WAIT_VMCNT(48);
+  else if (n >= 40) MUON_WAIT_VMCNT(40);
+  else if (n >= 32) MUON_WAIT_VMCNT(32);
+  else if (n >= 28) MUON_WAIT_VMCNT(28);
+  else if (n >= 24) MUON_WAIT_VMCNT(24);
+  else if (n >= 20) MUON_WAIT_VMCNT(20);
+  else if (n >= 16) MUON_WAIT_VMCNT(16);
+  else if (n >= 12) MUON_WAIT_VMCNT(12);
+  else if (n >= 8) MUON_WAIT_VMCNT(8);
+  else if (n >= 6) MUON_WAIT_VMCNT(6);
+  else if (n >= 4) MUON_WAIT_VMCNT(4);
+  else MUON_WAIT_VMCNT(0);
+}
+
+// Epilogue of one wave over its eight 32 x 32 accumulator blocks (b = 2 mi +
+// nj).  Inputs per block (A of stage 2 at the direct positions, W of the
+// weight step) are requested kDepth blocks ahead.
+template <int STAGE, int MODE>
+struct Epi {
+  static constexpr bool kUpd = STAGE == 3;
+  static constexpr bool kLastIt = kUpd && (MODE & kLast);
+  static constexpr bool kLoOut = kUpd && !kLastIt && (MODE & kWriteLo);
+  static constexpr int kDepth = STAGE == 2 ? 3 : (kLastIt ? 2 : 0);
+  static constexpr int kInSlots = kDepth > 0 ? kDepth : 1;
+  struct In {
+    u32x4 v[4];  // stage 2: A of row passes 0, 1 (bf16); weight step: W as fp32 bit patterns
+  };
+
+  int R0, C0;    // the wave's canonical origin
+  int lane, t;
+  float cb, cc, pre;
+  void* out;     // stage 1: A; stage 2: B; stage 3: the new X
+  uint8_t* xlo;
+  const void* ain;
+  uint32_t mp, np;
+  int transposed;
+  WRes w;
+  int sub, tj;   // 128-row subtile of the wave's rows; 128-column tile
+
+  __device__ __forceinline__ Epi(const StageArgs& args, const DevMat* m, const Ctx& c, int wm, int wn, int lane_)
+      : lane(lane_) {
+    R0 = c.i0 + 128 * wm;
+    C0 = c.j0 + 64 * wn;
+    sub = R0 >> 7;
+    tj = c.j0 >> 7;
+    t = args.t;
+    cb = args.b;
+    cc = args.c;
+    pre = 1.f;
+    if (args.t == 1 && STAGE != 3) {  // the first iteration works on U = X0 / s (s = 1 / (||U|| + eps))
+      const float s = load_uniform(load_uniform(&m->sc));
+      if (STAGE == 1) pre = s * s;
+      if (STAGE == 2) cb *= s, cc *= s;
+    }
+    mp = (uint32_t)load_uniform(&m->mp);
+    np = (uint32_t)load_uniform(&m->np);
+    xlo = nullptr;
+    ain = nullptr;
+    out = nullptr;
+    transposed = 0;
+    if (STAGE == 1) out = load_uniform(&m->a);
+    if (STAGE == 2) out = load_uniform(&m->b), ain = c.q;
+    if (STAGE == 3 && !kLastIt) {
+      out = (args.t & 1) ? load_uniform(&m->xo[1]) : load_uniform(&m->xo[0]);
+      if (kLoOut) xlo = load_uniform(&m->xlo);
+    }
+    if (kLastIt) {
+      transposed = load_uniform(&m->transposed);
+      w.bf16 = load_uniform(&m->w_bf16);
+      w.rows = load_uniform(&m->rows);
+      w.cols = load_uniform(&m->cols);
+      w.fast = !w.bf16 && load_uniform(&m->vec_w);
+      w.lr = args.lr * load_uniform(&m->scale);
+      w.r = make_rsrc(load_uniform(&m->w), (uint32_t)w.rows * (uint32_t)w.cols * (w.bf16 ? 2u : 4u));
+    }
+  }
+
+  __device__ __forceinline__ int br(int b) const { return R0 + 32 * (b >> 1); }
+  __device__ __forceinline__ int bc(int b) const { return C0 + 32 * (b & 1); }
+
+  // block kinds of the symmetric products
+  enum { kOff = 0, kDiag = 1, kLower = 2 };
+  __device__ __forceinline__ int kind(int b) const {
+    if (sub < tj) return kOff;
+    const int dr = 32 * (b >> 1), dc = (C0 & 127) + 32 * (b & 1);  // offsets in the diagonal subtile
+    return dr < dc ? kOff : dr == dc ? kDiag : kLower;
+  }
+
+  // vector-memory instructions of one block's input requests and of its stores
+  __device__ __forceinline__ int loads_per_block() const {
+    if (STAGE == 2) return 2;
+    if (kLastIt) return w.fast ? 4 : 0;
+    return 0;
+  }
+  __device__ __forceinline__ int stores_per_block() const {
+    if (STAGE != 3) return 6;
+    if (!kLastIt) return kLoOut ? 4 : 2;
+    return w.fast ? 4 : 0;
+  }
+
+  __device__ __forceinline__ void load(int b, In& in) const {
+    if (STAGE == 2) {
+      const uint32_t t0 = tiled(br(b), bc(b), mp);  // the block: 2 KiB contiguous
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        in.v[p] = *gv<u32x4>((const uint16_t*)ain + t0 + rp_row(p, lane) * 32 + rp_col(lane));
+    }
+    if (kLastIt && w.fast) {
+      if (!transposed) {  // W row = canonical row: row pass p, halves h
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            in.v[2 * p + h] = wload4(w, br(b) + rp_row(p, lane), bc(b) + rp_col(lane) + 4 * h);
+      } else {  // W row = canonical column: block pass, f = 0..3
+#pragma unroll
+        for (int f = 0; f < 4; ++f) in.v[f] = wload4(w, bc(b) + bp_col(lane) + f, br(b) + bp_row(lane));
+      }
+    }
+  }
+
+  __device__ __forceinline__ void process(int b, const Stage& st, const In& in) const {
+    const int r0 = br(b), c0 = bc(b);
+    if (kUpd) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int r = rp_row(p, lane), c = rp_col(lane);
+        float v[8];
+        read8(st, r, c, v);
+        if (!kLastIt) {
+          const uint32_t off = tiled(r0, c0, np) + r * 32 + c;  // the block: 2 KiB contiguous
+          const u32x4 hi = pack8_bf16(v);
+          __builtin_nontemporal_store(hi, gv<u32x4>((uint16_t*)out + off));
+          if (kLoOut) __builtin_nontemporal_store(lo8(v, hi), gv<u32x2>(xlo + off));
+        } else if (w.fast && !transposed) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            float wv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wv[e] = fmaf(-w.lr, v[4 * h + e], __uint_as_float(in.v[2 * p + h][e]));
+            wstore4(w, r0 + r, c0 + c + 4 * h, wv);
+          }
+        }
+      }
+      if (kLastIt && !w.fast) {  // any other W: element by element, lanes along W's rows
+#pragma unroll 1
+        for (int q = 0; q < 16; ++q) {
+          const int i = lane + 64 * q, a = i >> 5, b2 = i & 31;
+          const int r = transposed ? b2 : a, c = transposed ? a : b2;
+          const float o = *st.elem(r, c);
+          if (transposed)
+            wstep1(w, c0 + c, r0 + r, o);
+          else
+            wstep1(w, r0 + r, c0 + c, o);
+        }
+      }
+      if (kLastIt && w.fast && transposed) {
+        float blk[4][4];
+        read_block(st, bp_row(lane), bp_col(lane), blk);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          float wv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wv[e] = fmaf(-w.lr, blk[e][f], __uint_as_float(in.v[f][e]));
+          wstore4(w, c0 + bp_col(lane) + f, r0 + bp_row(lane), wv);
+        }
+      }
+      return;
+    }
+    // stages 1 and 2: A or B, written at (i, j) and at (j, i)
+    const int k = kind(b);
+    if (k == kDiag) symmetrize(st, lane);
+    const rsrc_t o_rs = make_rsrc(out, mp * mp * 2u);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int r = rp_row(p, lane), c = rp_col(lane);
+      float v[8];
+      read8(st, r, c, v);
+      if (STAGE == 1) {
+        if (t == 1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] *= pre;
+        }
+      } else {
+        float av[8];
+        unpack8_bf16(in.v[p], av);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = fmaf(cc, v[e], cb * av[e]);
+      }
+      const uint32_t o = k != kLower ? (tiled(r0, c0, mp) + r * 32 + c) * 2u : kOob;
+      store_b128(o_rs, o, pack8_bf16(v));
+      if (STAGE == 2 || t == 1) write8(st, r, c, v);  // the mirrored writes take the final values
+    }
+    float blk[4][4];
+    const int r = bp_row(lane), c = bp_col(lane);
+    read_block(st, r, c, blk);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const uint32_t o = k == kOff ? (tiled(c0, r0, mp) + (c + f) * 32 + r) * 2u : kOob;
+      store_b64(o_rs, o, pack4_bf16(blk[0][f], blk[1][f], blk[2][f], blk[3][f]));
+    }
+  }
+
+  // The whole epilogue.  `vm_pre`: vector-memory instructions issued after
+  // the requests of blocks 0 .. kDepth - 1 (made during the tile's last
+  // slabs).  Block b + kDepth's inputs are requested once block b has been
+  // processed (its input registers are then free).  Returns the instructions
+  // the epilogue itself issued.
+  __device__ __forceinline__ int run(const f32x16 (&acc)[4][2], const Stage& st, In (&in)[kInSlots],
+                                     int vm_pre) const {
+    const int lpb = loads_per_block(), spb = stores_per_block();
+    int issued = 0;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      st.put(acc[b >> 1][b & 1], lane);
+      if (kDepth > 0 && lpb > 0) {
+        // instructions issued after block b's request, which may stay in flight
+        int after;
+        if (b < kDepth) {
+          after = (kDepth - 1 - b) * lpb + vm_pre + issued;
+        } else {
+          const int last_req = b + kDepth - 1 < 8 ? b + kDepth - 1 : 7;
+          after = (kDepth - 1) * spb + (last_req - b) * lpb;
+        }
+        wait_vm(after);
+      }
+      process(b, st, in[b % kInSlots]);
+      issued += spb;
+      if (kDepth > 0 && lpb > 0 && b + kDepth < 8) {
+        load(b + kDepth, in[(b + kDepth) % kInSlots]);
+        issued += lpb;
+      }
+    }
+    return issued;
+  }
+};
+
+// Persistent product kernel: block b takes the table entries b, b + G,
+// b + 2 G, ... (G = gridDim.x, a multiple of 8: every entry stays on the XCD
+// the table placed it on).
+template <int STAGE, int MODE>
+__global__ __launch_bounds__(kThreads, kBlocks) void ns_bf16_kernel(StageArgs args) {
+  using E = Epi<STAGE, MODE>;
+  constexpr bool kLoIn = STAGE == 3 && (MODE & kHiLo);
+  constexpr int kDepth = E::kDepth;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int w = __builtin_amdgcn_readfirstlane(wave);
+  const int lane = threadIdx.x & 63;
+  const int stride = gridDim.x;
+  const FragOff fo = frag_off(lane);
+
+  uint64_t raw = 0;
+  int q = next_entry(args, blockIdx.x, stride, raw);
+  if (q >= args.ntiles) return;
+  Tile tl = tile_of(raw);
+  Ctx c = ctx_of<STAGE, MODE>(args, tl);
+  if (kLoIn) issue_lo(smem, c, 0, 0, w, lane);
+  issue_slab<STAGE>(smem, c, 0, 0, w, lane);
+  issue_slab<STAGE>(smem, c, 1, 1, w, lane);
+  int g = 0;     // slabs consumed by this block so far (ring slot g % 3, low-byte buffer g % 2)
+  int pend = 0;  // the previous epilogue's instructions, issued after this tile's first two slabs
+  for (;;) {
+    // the block's next tile, for the requests that run ahead into it
+    uint64_t rawn = 0;
+    const int qn = next_entry(args, q + stride, stride, rawn);
+    const bool more = qn < args.ntiles;
+    const Tile tn = tile_of(rawn);
+    Ctx cn = c;
+    if (more)
+      cn = ctx_of<STAGE, MODE>(args, tn);
+    else
+      cn.p = nullptr;  // empty requests keep the wait counts static
+    // waves whose rows lie wholly below the diagonal (stages 1 and 2) only move data
+    const bool idle = STAGE != 3 && (wm == 1 && c.skip1);
+    const int psrc = c.psrc;
+    const int R0 = c.i0 + 128 * wm;
+    float alpha = args.a;
+    if (STAGE == 3 && args.t == 1) alpha *= load_uniform(load_uniform(&args.mats[tl.mat].sc));
+    typename E::In in[E::kInSlots];
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < 2; ++nj)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[mi][nj][v] = 0.f;
+
+    const int nk = c.nk;
+    int vm_pre = 0;  // instructions issued after the epilogue's early input requests
+    for (int kt = 0; kt < nk; ++kt) {
+      // this wave's part of slab kt (and its low bytes) has landed: only slab
+      // kt + 1's requests may still be in flight, plus, at the first slabs of
+      // a tile, the previous epilogue's stores
+      if (kt == 0 || (kt == 1 && !kLoIn))
+        wait_vm(kDma + pend);
+      else
+        MUON_WAIT_VMCNT(kDma);
+      MUON_LDS_BARRIER();  // every wave's part has landed; slab kt - 1's slot is free
+      if (kLoIn) issue_lo(smem, kt + 1 < nk ? c : cn, kt + 1 < nk ? kt + 1 : kt + 1 - nk, (g + 1) & 1, w, lane);
+      if (STAGE == 2 && kt == nk - 2 && !idle) {  // the epilogue's first inputs
+        const E ep(args, args.mats + tl.mat, c, wm, wn, lane);
+#pragma unroll
+        for (int b = 0; b < kDepth; ++b) ep.load(b, in[b % E::kInSlots]);
+      }
+      const int slot = (g + 2) % kRing;
+      if (kt + 2 < nk)
+        issue_slab<STAGE>(smem, c, kt + 2, slot, w, lane);
+      else
+        issue_slab<STAGE>(smem, cn, kt + 2 - nk, slot, w, lane);
+      if (STAGE == 2 && kt >= nk - 2) vm_pre += kDma;
+      const char* s = smem + (g % kRing) * kSlot;
+      if (!idle) {
+        const char* p = psrc ? s + (psrc - 1) * kHalf : s + 2 * kHalf;
+        if (STAGE == 3) {
+          const int rel = kt * kBK - R0;  // this slab's K rows are output rows of the wave
+          if (rel >= 0 && rel < 128) {
+            const char* lo = smem + kLoBase + (g & 1) * kLoBuf;
+            switch (rel >> 5) {
+              case 0: fold_x<kLoIn>(acc[0], p, lo, wn, lane, alpha); break;
+              case 1: fold_x<kLoIn>(acc[1], p, lo, wn, lane, alpha); break;
+              case 2: fold_x<kLoIn>(acc[2], p, lo, wn, lane, alpha); break;
+              default: fold_x<kLoIn>(acc[3], p, lo, wn, lane, alpha); break;
+            }
+          }
+        }
+        mma_slab<STAGE == 3>(acc, s + wm * kHalf, p, wn, lane, fo);
+      }
+      ++g;
+    }
+
+    // epilogue: the last slab's slot holds the waves' staged blocks
+    MUON_LDS_BARRIER();  // all waves are done with the last slab
+    pend = 0;
+    if (!idle) {
+      const E ep(args, args.mats + tl.mat, c, wm, wn, lane);
+      int early = 0;  // requests made after the next tile's first slabs, before run()
+      if (E::kLastIt) {  // the weight step requests its first W blocks here (registers are short in the loop)
+#pragma unroll
+        for (int b = 0; b < kDepth; ++b) ep.load(b, in[b % E::kInSlots]);
+        vm_pre = 0;
+        early = kDepth * ep.loads_per_block();
+      }
+      Stage st;
+      st.base = smem + ((g + kRing - 1) % kRing) * kSlot + w * kBlock;
+      pend = early + ep.run(acc, st, in, vm_pre);
+    }
+    if (!more) break;
+    q = qn;
+    tl = tn;
+    c = cn;
+  }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ launchers --
+#define MUON_BF16_KERNEL(S, M) ((const void*)ns_bf16_kernel<S, M>)
+
+hipError_t prepare_bf16_kernels() {
+  const void* fns[] = {MUON_BF16_KERNEL(1, 0), MUON_BF16_KERNEL(2, 0), MUON_BF16_KERNEL(3, 0),
+                       MUON_BF16_KERNEL(3, 1), MUON_BF16_KERNEL(3, 5), MUON_BF16_KERNEL(3, 2),
+                       MUON_BF16_KERNEL(3, 3)};
+  for (const void* f : fns) {
+    hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+static hipError_t launch_bf16(const void* fn, int blocks, const StageArgs& args, hipStream_t stream, hipEvent_t ev0,
+                              hipEvent_t ev1) {
+  void* kargs[] = {(void*)&args};
+  return hipExtLaunchKernel(fn, dim3(blocks), dim3(kThreads), kargs, kLds, stream, ev0, ev1, 0);
+}
+
+hipError_t launch_stage_bf16(int stage, const StageArgs& args, int blocks, hipStream_t stream, hipEvent_t ev0,
+                             hipEvent_t ev1) {
+  const bool last = args.t == args.T;
+  const bool hilo = args.t <= args.kmaster;
+  const bool write_lo = !last && args.t < args.kmaster;
+  const void* fn = nullptr;
+  if (stage == 1) fn = MUON_BF16_KERNEL(1, 0);
+  if (stage == 2) fn = MUON_BF16_KERNEL(2, 0);
+  if (stage == 3) {
+    if (last)
+      fn = hilo ? MUON_BF16_KERNEL(3, 3) : MUON_BF16_KERNEL(3, 2);
+    else if (write_lo)
+      fn = MUON_BF16_KERNEL(3, 5);
+    else
+      fn = hilo ? MUON_BF16_KERNEL(3, 1) : MUON_BF16_KERNEL(3, 0);
+  }
+  if (!fn) return hipErrorInvalidValue;
+  return launch_bf16(fn, blocks, args, stream, ev0, ev1);
+}
+
+}  // namespace muon

@@ -87,7 +87,8 @@ def describe(shapes: Sequence[Tuple[int, int]], path: str = "bf16", x_master_ite
         tiles = [tuple(buf[3 * q:3 * q + 3]) for q in range(count.value)]
     d = dict(workspace_bytes=info.workspace_bytes, n_matrices=info.n_matrices, tile=info.tile,
              blocks=list(info.blocks), x_master_iters=info.x_master_iters, path=info.path,
-             n_f32_matrices=info.n_f32_matrices, n_groups=info.n_groups)
+             n_f32_matrices=info.n_f32_matrices, n_groups=info.n_groups,
+             bf16_tile_rows=info.bf16_tile_rows, bf16_tile_cols=info.bf16_tile_cols)
     return d, tiles
 
 

@@ -37,12 +37,15 @@ from collections import defaultdict
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 # the kernels and the launch structure (api.hip decides which launches a step makes)
-KERNEL_SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kernels.hip", "muon_internal.h", "api.hip")]
+KERNEL_SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kernels.hip", "products.hip", "device_common.h", "muon_internal.h", "api.hip")]
 COPY_BYTES = 256 << 20  # bench.py --calibrate-copy: one plain copy of 256 MiB
 
 KINDS = {
     "momentum_kernel": "momentum",
     "norm_kernel": "norm",
+    "ns_bf16_kernel<1": "gram",
+    "ns_bf16_kernel<2": "poly",
+    "ns_bf16_kernel<3": "update",
     "ns_stage_kernel<1": "gram",
     "ns_stage_kernel<2": "poly",
     "ns_stage_kernel<3": "update",
