@@ -47,6 +47,14 @@
  * still in flight); inputs must stay alive until the stream has passed the
  * step.
  *
+ * Graph capture.  A step may be enqueued into a capturing stream (HIP stream
+ * capture); the graph then reads the plan's device copy of the matrix table
+ * as it stood at capture time, so from then on the plan's pointers are fixed:
+ * a step whose descriptors carry other pointers, during capture or after it,
+ * fails with MUON_E_INVAL (make a new plan for new buffers).  Profiling must
+ * be off while capturing (MUON_E_INVAL otherwise).  Replays and eager steps
+ * of the same plan must be ordered like any two steps of one plan.
+ *
  * Errors.  Every int-returning function returns MUON_OK (0) or a negative
  * MUON_E_* code and then sets a thread-local message readable with
  * muon_last_error().  No C++ exception crosses this ABI.  Gradient values are

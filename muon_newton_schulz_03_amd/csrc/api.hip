@@ -46,6 +46,8 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(MUON_E_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
 }
 
+void release(muon_plan* p);
+
 constexpr int kSlots = 8;           // device copies of the matrix table (pointer updates)
 constexpr size_t kAlign = 256;
 constexpr int kMaxMatrices = 65000; // tile tables index matrices with 16 bits
@@ -391,6 +393,7 @@ struct muon_plan {
   hipEvent_t slot_ev[kSlots] = {};
   bool slot_used[kSlots] = {};
   int slot = 0;
+  bool captured = false;  // a step of this plan was enqueued into a capturing stream
   hipEvent_t last_ev = nullptr;        // recorded after the last enqueued work
   bool last_valid = false;
   hipStream_t gs[kGroups] = {};        // the groups' Newton-Schulz streams (default priority)
@@ -629,7 +632,7 @@ int muon_init(const muon_matrix_desc* descs, int n, const muon_options* opts, vo
   hipStream_t stream = (hipStream_t)hip_stream;
 
   auto cleanup = [&](int code) {
-    muon_destroy(p);
+    release(p);
     return code;
   };
   for (int s = 0; s < kSlots; ++s) {
@@ -715,6 +718,11 @@ static int step_impl(muon_plan* p, const muon_matrix_desc* descs, int n, const f
   if (!std::isfinite(lr)) return fail(MUON_E_INVAL, "lr must be finite");
   if (!(momentum >= 0.f && momentum <= 1.f)) return fail(MUON_E_INVAL, "momentum %g outside [0, 1]", momentum);
   hipStream_t stream = (hipStream_t)hip_stream;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t ce = hipStreamIsCapturing(stream, &cap);
+  if (ce != hipSuccess) return hip_fail(ce, "hipStreamIsCapturing");
+  const bool capturing = cap != hipStreamCaptureStatusNone;
+  if (capturing && p->prof) return fail(MUON_E_INVAL, "profiling is on: a timed step cannot be captured in a graph");
 
   bool changed = false;
   if (descs) {
@@ -729,6 +737,11 @@ static int step_impl(muon_plan* p, const muon_matrix_desc* descs, int n, const f
         return fail(MUON_E_MISMATCH, "matrix %d: shape, dtype or scale differs from the plan", i);
       if (x.weight != y.weight || x.grad != y.grad || x.momentum != y.momentum) changed = true;
     }
+    if (changed && (capturing || p->captured))
+      return fail(MUON_E_INVAL,
+                  "matrix pointers changed %s: a captured step reads the plan's matrix table, which a pointer "
+                  "change rewrites; use a new plan for new buffers",
+                  capturing ? "while the stream is capturing a graph" : "after a step of this plan was captured");
     if (changed) {
       for (int i = 0; i < n; ++i) {
         p->desc[i].weight = descs[i].weight;
@@ -817,6 +830,7 @@ static int step_impl(muon_plan* p, const muon_matrix_desc* descs, int n, const f
       if (e != hipSuccess) return hip_fail(e, "join of the group streams");
     }
   }
+  if (capturing) p->captured = true;
   return note_slot_use(p, stream);
 }
 
@@ -834,9 +848,11 @@ int muon_step_schedule(muon_plan* p, const muon_matrix_desc* descs, int n, const
   return step_impl(p, descs, n, coeffs, 0.f, 0.f, 0.f, T, momentum, nesterov, lr, hip_stream);
 }
 
-int muon_destroy(muon_plan* p) {
-  g_err.clear();
-  if (!p) return MUON_OK;
+namespace {
+// Frees a plan's host state; leaves the thread's error message alone (init's
+// failure paths call it after recording what failed).
+void release(muon_plan* p) {
+  if (!p) return;
   if (p->last_valid) (void)hipEventSynchronize(p->last_ev);
   for (int s = 0; s < kSlots; ++s) {
     if (p->host_slots[s]) (void)hipHostFree(p->host_slots[s]);
@@ -850,6 +866,12 @@ int muon_destroy(muon_plan* p) {
   }
   for (hipEvent_t ev : p->pev) (void)hipEventDestroy(ev);
   delete p;
+}
+}  // namespace
+
+int muon_destroy(muon_plan* p) {
+  g_err.clear();
+  release(p);
   return MUON_OK;
 }
 

@@ -109,3 +109,77 @@ def check_momentum(m_gpu: torch.Tensor, m_ref: np.ndarray, what: str):
 def update_from_weights(w_after, w_before, lr, scale=1.0):
     """O recovered from the weight change: (W_before - W_after) / (lr * s)."""
     return (np.asarray(w_before, np.float64) - np.asarray(w_after, np.float64)) / (O.f32(lr) * scale)
+
+
+@dataclass
+class StreamResult:
+    worst: Dict[int, float] = field(default_factory=dict)       # worst rel err of O per compared matrix
+    w_final: Dict[int, np.ndarray] = field(default_factory=dict)  # tracked: GPU weights after the last step
+    w_ref: Dict[int, np.ndarray] = field(default_factory=dict)    # tracked: oracle weights after the last step
+    compared: int = 0                                             # (matrix, step) pairs compared
+
+
+def stream_parity(shapes, grads_at, nsteps, *, check, track=(), path="bf16", T=5, mu=0.95, nesterov=True,
+                  lr=0.05, coeffs=(A, B, C), groups=0, tol=None) -> StreamResult:
+    """Run ``nsteps`` HIP steps over all ``shapes`` and compare as they go.
+
+    ``grads_at(t)`` returns step t's gradients (one tensor per matrix).  After
+    step t the matrices ``check(t)`` are compared with the oracle: O recovered
+    from the step's weight change (rel. Frobenius <= tol) and the momentum
+    buffer elementwise.  The oracle keeps state only for the matrices that are
+    ever checked or tracked: it advances their momentum every step and runs
+    the Newton-Schulz iteration at the steps that compare them; for the
+    ``track`` matrices it runs every step and keeps their weights, which are
+    returned with the GPU's after the last step.  Weights start at zero.
+    """
+    from muon_newton_schulz_03_amd import MuonStep
+
+    tol = tol if tol is not None else (TOL_F32 if path == "f32" else TOL_BF16)
+    dev = torch.device("cuda:0")
+    n = len(shapes)
+    track = set(track)
+    union = sorted(set().union(*[set(check(t)) for t in range(nsteps)]) | track)
+    W = [torch.zeros(s, dtype=torch.float32, device=dev) for s in shapes]
+    M = [torch.zeros(s, dtype=torch.float32, device=dev) for s in shapes]
+    g0 = grads_at(0)
+    G = [g.to(dev).clone().contiguous() for g in g0]
+    plan = MuonStep(W, G, M, path=path, groups=groups)
+    m_ref = {i: np.zeros(shapes[i], np.float32) for i in union}
+    w_ref = {i: np.zeros(shapes[i], np.float64) for i in track}
+    w_prev = {i: np.zeros(shapes[i], np.float32) for i in union}
+    res = StreamResult()
+    a, b, c = coeffs
+    for t in range(nsteps):
+        grads = g0 if t == 0 else grads_at(t)
+        if t > 0:
+            for i in range(n):
+                G[i].copy_(grads[i].to(dev))
+        plan.step(a=a, b=b, c=c, T=T, momentum=mu, nesterov=nesterov, lr=lr)
+        torch.cuda.synchronize()
+        want = set(check(t))
+        for i in union:
+            g = O.as_f64(grads[i].cpu())
+            w_now = W[i].cpu().numpy()
+            if i in want or i in track:
+                r = O.muon_step(w_ref[i] if i in track else np.zeros(shapes[i]), g, m_ref[i], a=a, b=b, c=c,
+                                T=T, mu=mu, nesterov=nesterov, lr=lr)
+                m_ref[i] = r.M
+                if i in track:
+                    w_ref[i] = r.W
+                if i in want:
+                    og = update_from_weights(w_now, w_prev[i], lr)
+                    e = O.rel_frobenius(og, r.O)
+                    res.worst[i] = max(res.worst.get(i, 0.0), e)
+                    res.compared += 1
+                    assert e <= tol, f"matrix {i} {shapes[i]} step {t}: rel err {e:.3e} > {tol}"
+                    check_momentum(M[i].cpu(), r.M, f"matrix {i} step {t}")
+            else:
+                m_ref[i] = O.momentum_update(m_ref[i], g, mu)
+            w_prev[i] = w_now
+        say(f"  step {t + 1}/{nsteps}: {len(want)} matrices compared, worst so far "
+            f"{max(res.worst.values()) if res.worst else 0.0:.3e}")
+    for i in track:
+        res.w_final[i] = W[i].cpu().numpy().astype(np.float64)
+        res.w_ref[i] = w_ref[i]
+    plan.close()
+    return res

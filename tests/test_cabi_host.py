@@ -287,3 +287,18 @@ def test_binding_rejects_host_tensors():
     w = torch.zeros(4, 4)
     with pytest.raises(ValueError, match="device"):
         MuonStep([w], [w.clone()], [w.clone()])
+
+
+def test_init_reports_hip_failures(lib):
+    """Where a HIP runtime call fails (here: no device at all), muon_init returns
+    MUON_E_HIP, names the call and keeps the runtime's own message."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a device is present: this case needs a host without one")
+    plan = ctypes.c_void_p()
+    ok = descs([(64, 64)], True)
+    ws = lib.muon_workspace_size(ok, 1, None)
+    expect_error(_lib.MUON_E_HIP, lib.muon_init, ok, 1, None, ctypes.c_void_p(0x10000000), ws, None,
+                 ctypes.byref(plan), match=r"^hip\w+\(.*\): .+ \(\d+\)$")
+    assert not plan.value
+    assert "device" in _lib.last_error()

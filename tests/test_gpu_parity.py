@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from muon_harness import (A, B, C, TOL_BF16, TOL_F32, O, check_momentum, oracle_steps, run_gpu, say,
-                          update_from_weights)
+                          stream_parity, update_from_weights)
 from muon_newton_schulz_03_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -70,72 +70,111 @@ def test_single768_bf16_path_too():
     say(f"  rel err {worst:.3e}")
 
 
+@pytest.mark.timeout(1200)
 def test_gpt2_small_ten_steps():
-    """72 matrices, 10 consecutive steps; one layer's six matrices checked at every step."""
-    say("[gpu] gpt2_small 10 steps")
+    """72 matrices, 10 consecutive steps with fresh gradients: every matrix is
+    compared at every step, and the total weight change after the 10 steps."""
+    say("[gpu] gpt2_small 10 steps, all 72 matrices")
     wl = inputs.workload("gpt2_small")
-    steps = [inputs.gradients("gpt2_small", t) for t in range(wl.steps)]
-    sample = [0, 3, 4, 5, 66, 71]
-    gpu = run_gpu(wl.shapes, steps, path="bf16", lr=wl.lr, sample=sample)
-    worst = compare_run(wl.shapes, steps, gpu, path="bf16", lr=wl.lr, mu=wl.momentum, nesterov=True,
-                        sample=sample)
-    say(f"  worst rel err {worst:.3e}")
+    n = len(wl.shapes)
+    res = stream_parity(wl.shapes, lambda t: inputs.gradients("gpt2_small", t), wl.steps,
+                        check=lambda t: range(n), track=range(n), lr=wl.lr, mu=wl.momentum)
+    assert res.compared == n * wl.steps
+    say(f"  worst rel err over {res.compared} (matrix, step) pairs {max(res.worst.values()):.3e}")
+    num = den = 0.0
+    for i in range(n):  # weights started at zero: W after 10 steps is the total change
+        e = O.rel_frobenius(res.w_final[i], res.w_ref[i])
+        assert e <= TOL_BF16, f"matrix {i}: total weight change after 10 steps rel err {e:.3e}"
+        num += float(np.sum((res.w_final[i] - res.w_ref[i]) ** 2))
+        den += float(np.sum(res.w_ref[i] ** 2))
+    say(f"  total weight change over the set after 10 steps: rel err {np.sqrt(num / den):.3e}")
+    assert np.sqrt(num / den) <= TOL_BF16
 
 
+QUANTS = (0.0, 0.01, 0.5, 0.99, 1.0)  # min, p1, p50, p99, max
+
+
+def sigma_quantiles(x: np.ndarray) -> np.ndarray:
+    return np.quantile(np.linalg.svd(x, compute_uv=False), QUANTS)
+
+
+def polar_factor(g: np.ndarray) -> np.ndarray:
+    u, _, vt = np.linalg.svd(g, full_matrices=False)
+    return u @ vt
+
+
+@pytest.mark.timeout(900)
 def test_illconditioned():
+    """24 ill-conditioned 768x768 matrices, one step.  Every output is compared
+    with the oracle; the spread of its singular values (min, p1, p50, p99, max)
+    is reported and bounded against the oracle's, and its distance to the
+    polar factor U V^T of the input is reported beside the oracle's."""
     say("[gpu] illcond768")
     wl = inputs.workload("illcond768")
     steps = [inputs.gradients("illcond768", 0)]
     gpu = run_gpu(wl.shapes, steps, path="bf16", lr=1.0)
     worst = compare_run(wl.shapes, steps, gpu, path="bf16", lr=1.0, mu=0.95, nesterov=True)
     say(f"  worst rel err {worst:.3e}")
-    # singular-value spread of one output: same band as the oracle's
-    og = update_from_weights(gpu.W[0][0], np.zeros((768, 768)), 1.0)
-    ref = oracle_steps(torch.zeros(768, 768), [steps[0][0]], lr=1.0)[0].O
-    sg, sr = np.linalg.svd(og, compute_uv=False), np.linalg.svd(ref, compute_uv=False)
-    say(f"  sigma gpu [{sg.min():.4f}, {np.median(sg):.4f}, {sg.max():.4f}]"
-        f" oracle [{sr.min():.4f}, {np.median(sr):.4f}, {sr.max():.4f}]")
-    assert abs(sg.max() - sr.max()) < 0.02 and abs(np.median(sg) - np.median(sr)) < 0.02
+    say("  matrix  sigma(gpu) min/p1/p50/p99/max            sigma(oracle) min/p1/p50/p99/max         "
+        "rel_F to UV^T gpu / oracle")
+    dq_worst = 0.0
+    for i in range(len(wl.shapes)):
+        og = update_from_weights(gpu.W[0][i], np.zeros(wl.shapes[i]), 1.0)
+        ref = oracle_steps(torch.zeros(wl.shapes[i]), [steps[0][i]], lr=1.0)[0].O
+        qg, qr = sigma_quantiles(og), sigma_quantiles(ref)
+        # the first Nesterov step from zero momentum orthogonalises (1 + mu) G: U V^T of G
+        uv = polar_factor(O.as_f64(steps[0][i]))
+        dg, dr = O.rel_frobenius(og, uv), O.rel_frobenius(ref, uv)
+        say(f"  {i:6d}  " + " ".join(f"{v:.4f}" for v in qg) + "   " + " ".join(f"{v:.4f}" for v in qr)
+            + f"   {dg:.4f} / {dr:.4f}")
+        # singular values of nearby matrices differ by at most the spectral norm of the
+        # difference (Weyl), which the Frobenius distance bounds; the band the quintic
+        # targets is of unit scale, so each quantile must also agree within TOL_BF16
+        e = O.rel_frobenius(og, ref)
+        assert np.max(np.abs(qg - qr)) <= e * np.linalg.norm(ref) + 1e-9, (i, qg, qr)
+        assert np.max(np.abs(qg - qr)) <= TOL_BF16, (i, qg, qr)
+        assert abs(dg - dr) <= e * np.linalg.norm(ref) / np.linalg.norm(uv) + 1e-9
+        dq_worst = max(dq_worst, float(np.max(np.abs(qg - qr))))
+    say(f"  largest sigma-quantile difference gpu vs oracle {dq_worst:.3e}")
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("nesterov", [True, False])
 def test_aspect_ratio_transpose(nesterov):
+    """48 matrices alternating 3072x768 / 768x3072: all 48 compared at the
+    third step, two of each orientation at every step."""
     say(f"[gpu] aspect3072 nesterov={nesterov}")
     wl = inputs.workload("aspect3072")
     run = 0 if nesterov else 1
-    steps = [inputs.gradients("aspect3072", t, run=run) for t in range(wl.steps)]
-    sample = [0, 1, 46, 47]
-    gpu = run_gpu(wl.shapes, steps, path="bf16", lr=1.0, nesterov=nesterov, sample=sample)
-    worst = compare_run(wl.shapes, steps, gpu, path="bf16", lr=1.0, mu=0.95, nesterov=nesterov, sample=sample)
-    say(f"  worst rel err {worst:.3e}")
+    n = len(wl.shapes)
+    last = wl.steps - 1
+    res = stream_parity(wl.shapes, lambda t: inputs.gradients("aspect3072", t, run=run), wl.steps,
+                        check=lambda t: range(n) if t == last else [0, 1, 46, 47], lr=1.0, nesterov=nesterov)
+    assert len(res.worst) == n
+    say(f"  worst rel err {max(res.worst.values()):.3e} over {res.compared} (matrix, step) pairs")
 
 
+@pytest.mark.timeout(1200)
 def test_width1024_fifty_steps():
-    """144 matrices, 50 steps with state kept on device; sampled matrices checked at
-    steps 1, 2, 10, 25, 50 and the weight change of one matrix after all 50."""
+    """144 matrices, 50 steps with the state kept on device: matrices of every
+    shape from both plan groups (layers 0 and 23) compared at steps 1, 2, 10, 25
+    and 50, and the weights of one matrix per group after all 50 steps."""
     say("[gpu] width1024 50 steps")
     wl = inputs.workload("width1024")
-    dev = "cuda:0"
+    from muon_newton_schulz_03_amd.muon import describe
+    info, _ = describe(wl.shapes)
+    assert info["n_groups"] == 2
     check_steps = {0, 1, 9, 24, 49}
-    sample = [0, 4, 5]
-    steps = [inputs.gradients("width1024", t, device=dev) for t in range(wl.steps)]
-    keep = sorted(check_steps | {t - 1 for t in check_steps if t > 0})
-    gpu = run_gpu(wl.shapes, steps, path="bf16", lr=wl.lr, sample=sample, keep_steps=keep)
-    for si, i in enumerate(sample):
-        say(f"  oracle for matrix {i} {wl.shapes[i]}")
-        grads = [steps[t][i].cpu() for t in range(wl.steps)]
-        need = check_steps if si > 0 else None  # matrix 0: the full 50-step oracle
-        ref = oracle_steps(torch.zeros(wl.shapes[i]), grads, lr=wl.lr, need_ns=need)
-        for t in sorted(check_steps):
-            prev = np.zeros(wl.shapes[i]) if t == 0 else gpu.W[t - 1][si]
-            og = update_from_weights(gpu.W[t][si], prev, wl.lr)
-            e = O.rel_frobenius(og, ref[t].O)
-            assert e <= TOL_BF16, f"matrix {i} step {t}: {e:.3e}"
-            check_momentum(gpu.M[t][si], ref[t].M, f"matrix {i} step {t}")
-        if si == 0:
-            e = O.rel_frobenius(-gpu.W[49][0], -ref[49].W)
-            say(f"  matrix 0 weight after 50 steps rel err {e:.3e}")
-            assert e <= TOL_BF16
+    sample = [0, 4, 5, 72, 76, 77, 142, 143]
+    track = [0, 143]
+    res = stream_parity(wl.shapes, lambda t: inputs.gradients("width1024", t, device="cuda:0"), wl.steps,
+                        check=lambda t: sample if t in check_steps else [], track=track, lr=wl.lr)
+    assert sorted(res.worst) == sample and res.compared == len(sample) * len(check_steps)
+    say("  worst rel err per matrix: " + ", ".join(f"{i}: {res.worst[i]:.2e}" for i in sample))
+    for i in track:
+        e = O.rel_frobenius(res.w_final[i], res.w_ref[i])
+        say(f"  matrix {i} {wl.shapes[i]} weights after 50 steps rel err {e:.3e}")
+        assert e <= TOL_BF16
 
 
 def test_determinism_and_grouping():
@@ -346,6 +385,9 @@ def test_graph_capture_replays_match_eager(groups):
     torch.cuda.synchronize()
     for w in Wg + Mg:
         assert torch.count_nonzero(w).item() == 0  # capture ran nothing
+    # the oracle over the same four steps (the gradient buffers keep their values)
+    refs = [oracle_steps(torch.zeros(s), [G[i].cpu()] * 4, lr=kw["lr"]) for i, s in enumerate(shapes)]
+    prev = [np.zeros(s) for s in shapes]
     for rep in range(4):
         pe.step(**kw)
         graph.replay()
@@ -353,6 +395,43 @@ def test_graph_capture_replays_match_eager(groups):
         torch.cuda.synchronize()
         for i in range(len(shapes)):
             assert torch.equal(We[i], Wg[i]) and torch.equal(Me[i], Mg[i]), f"replay {rep} matrix {i}"
+            w = Wg[i].cpu().double().numpy()
+            e = O.rel_frobenius(update_from_weights(w, prev[i], kw["lr"]), refs[i][rep].O)
+            assert e <= TOL_BF16, f"replay {rep} matrix {i}: rel err {e:.3e} against the oracle"
+            check_momentum(Mg[i].cpu(), refs[i][rep].M, f"replay {rep} matrix {i}")
+            prev[i] = w
         assert torch.isfinite(scratch)
+    # the captured plan's pointers are fixed: new buffers are refused, eagerly and under capture
+    from muon_newton_schulz_03_amd._lib import MUON_E_INVAL, MuonError
+    other = [torch.zeros(s, device=dev) for s in shapes]
+    with pytest.raises(MuonError, match="captured") as err:
+        pg.step(weights=other, **kw)
+    assert err.value.code == MUON_E_INVAL
+    g2 = torch.cuda.CUDAGraph()
+    with pytest.raises(MuonError, match="capturing"):
+        with torch.cuda.graph(g2):
+            torch.ones(4, device=dev).mul_(2)  # the graph is not empty when the step is refused
+            pe.step(weights=other, **kw)
+    torch.cuda.synchronize()
     pe.close()
     pg.close()
+
+
+def test_nan_gradient_stays_in_its_matrix():
+    """A NaN in one gradient reaches that matrix's momentum (at that entry only)
+    and its weights; every other matrix of the plan is bitwise unchanged."""
+    say("[gpu] NaN gradient isolation")
+    shapes = [(256, 384), (384, 256), (200, 200), (768, 768)]
+    clean = [[inputs.custom_gradient(r, c, 1200 + i) for i, (r, c) in enumerate(shapes)]]
+    bad = [[g.clone() for g in clean[0]]]
+    bad[0][1][17, 5] = float("nan")
+    for groups in (1, 2):
+        ref = run_gpu(shapes, clean, lr=0.1, groups=groups)
+        got = run_gpu(shapes, bad, lr=0.1, groups=groups)
+        for i in (0, 2, 3):
+            assert torch.equal(got.W[0][i], ref.W[0][i]) and torch.equal(got.M[0][i], ref.M[0][i]), (groups, i)
+        m_nan = torch.isnan(got.M[0][1])
+        assert m_nan[17, 5] and int(m_nan.sum()) == 1
+        keep = ~m_nan
+        assert torch.equal(got.M[0][1][keep], ref.M[0][1][keep])
+        assert torch.isnan(got.W[0][1]).all()
