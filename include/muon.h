@@ -159,6 +159,26 @@ int muon_step(muon_plan* plan, const muon_matrix_desc* descs, int n, float a, fl
 int muon_step_schedule(muon_plan* plan, const muon_matrix_desc* descs, int n, const float* coeffs, int T,
                        float momentum, int nesterov, float lr, void* hip_stream);
 
+/* For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid hipMalloc): one muon_step over
+ * the n descriptors without a plan or a workspace.  The working memory (X
+ * copies, A, B, partial sums, tables) is a static device array of 64 MiB
+ * (MUON_SCRATCH_BYTES) that the library holds on every GPU it runs on until
+ * the process ends; the call allocates nothing.  It plans on the host each
+ * time, copies the tables into that array from pageable host memory on
+ * hip_stream and enqueues the step there (groups is ignored: one stream).
+ * Arguments are those of muon_init (opts: path, x_master_iters and max_T;
+ * zero_momentum must be 0) and muon_step; the stream must belong to the
+ * current device.  A set whose working memory exceeds the array fails with
+ * MUON_E_WORKSPACE (muon_workspace_size gives the need, within a few KiB).
+ * All calls on one GPU share its array and every call rewrites what it reads
+ * before reading it, so only overlap matters: calls that can run at the same
+ * time on one GPU (other streams, other host threads) race and must be
+ * ordered by the caller. */
+#define MUON_SCRATCH_BYTES (64u << 20)
+int muon_step_scratch(const muon_matrix_desc* descs, int n, const muon_options* opts, float a, float b, float c,
+                      int T, float momentum, int nesterov, float lr, void* hip_stream);
+
 /* Free the plan's host state.  The workspace stays the caller's. */
 int muon_destroy(muon_plan* plan);
 

@@ -12,6 +12,7 @@ MUON_E_INVAL = -1
 MUON_E_UNSUPPORTED = -2
 MUON_E_MISMATCH = -3
 MUON_E_WORKSPACE = -4
+MUON_SCRATCH_BYTES = 64 << 20
 MUON_E_HIP = -5
 
 MUON_DTYPE_F32 = 0
@@ -24,7 +25,8 @@ KIND_COUNT = 6
 KIND_NAMES = ("momentum", "gram", "poly", "update", "apply", "norm")
 
 EXPORTS = ("muon_version", "muon_workspace_size", "muon_init", "muon_step", "muon_step_schedule", "muon_destroy",
-           "muon_last_error", "muon_describe", "muon_profile_enable", "muon_profile_select", "muon_profile_read")
+           "muon_last_error", "muon_describe", "muon_profile_enable", "muon_profile_select", "muon_profile_read",
+           "muon_step_scratch")
 
 
 class MatrixDesc(ctypes.Structure):
@@ -81,6 +83,10 @@ def load() -> ctypes.CDLL:
     lib.muon_step_schedule.restype = ctypes.c_int
     lib.muon_step_schedule.argtypes = [ctypes.c_void_p, P(MatrixDesc), ctypes.c_int, P(ctypes.c_float), ctypes.c_int,
                                        ctypes.c_float, ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
+    lib.muon_step_scratch.restype = ctypes.c_int
+    lib.muon_step_scratch.argtypes = [P(MatrixDesc), ctypes.c_int, P(Options), ctypes.c_float, ctypes.c_float,
+                                      ctypes.c_float, ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_float,
+                                      ctypes.c_void_p]
     lib.muon_destroy.restype = ctypes.c_int
     lib.muon_destroy.argtypes = [ctypes.c_void_p]
     lib.muon_describe.restype = ctypes.c_int

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -704,6 +705,9 @@ int muon_init(const muon_matrix_desc* descs, int n, const muon_options* opts, vo
 }
 
 // One step; iteration t uses sched[3(t-1) .. 3(t-1)+2] when sched is given, else (a, b, c).
+static int enqueue_step(muon_plan* p, const DevMat* mats, const float* sched, float a, float b, float c, int T,
+                        float momentum, int nesterov, float lr, hipStream_t stream);
+
 static int step_impl(muon_plan* p, const muon_matrix_desc* descs, int n, const float* sched, float a, float b,
                      float c, int T, float momentum, int nesterov, float lr, void* hip_stream) {
   g_err.clear();
@@ -754,7 +758,16 @@ static int step_impl(muon_plan* p, const muon_matrix_desc* descs, int n, const f
     }
   }
 
-  const DevMat* mats = slot_ptr(p, p->slot);
+  int rc = enqueue_step(p, slot_ptr(p, p->slot), sched, a, b, c, T, momentum, nesterov, lr, stream);
+  if (rc) return rc;
+  if (capturing) p->captured = true;
+  return note_slot_use(p, stream);
+}
+
+// Enqueue one step's launches over the plan's matrices (table `mats`, already
+// on the device) on `stream`.
+static int enqueue_step(muon_plan* p, const DevMat* mats, const float* sched, float a, float b, float c, int T,
+                        float momentum, int nesterov, float lr, hipStream_t stream) {
   static const int kKinds[3] = {MUON_KIND_GRAM, MUON_KIND_POLY, MUON_KIND_UPDATE};
   static const char* kNames[3] = {"gram launch", "poly launch", "update launch"};
   LaunchEvents ev;
@@ -830,8 +843,7 @@ static int step_impl(muon_plan* p, const muon_matrix_desc* descs, int n, const f
       if (e != hipSuccess) return hip_fail(e, "join of the group streams");
     }
   }
-  if (capturing) p->captured = true;
-  return note_slot_use(p, stream);
+  return MUON_OK;
 }
 
 int muon_step(muon_plan* p, const muon_matrix_desc* descs, int n, float a, float b, float c, int T, float momentum,
@@ -912,3 +924,108 @@ int muon_profile_read(muon_plan* p, double* ms, int64_t* launches) {
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------- allocation-free step --
+//
+// The step's working memory (X copies, A, B, partial sums, tables) lives in
+// this file-scope array instead of a caller workspace.  Every GPU the library
+// runs on holds its own copy, from module load to the end of the process.
+// Host code never passes the array's name to a kernel or a copy: it passes
+// the device address taken once per device with hipGetSymbolAddress.
+namespace {
+constexpr size_t kScratchBytes = MUON_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};      // device address of `scratch`, per device
+std::vector<char> g_scratch_host[kMaxDevices];  // pageable staging of the tables, per device
+
+// Device address of the current device's scratch array (taken on the first
+// call on that device, with the device current) and its host staging buffer.
+int scratch_for_current_device(void** dev_ptr, std::vector<char>** host) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MUON_E_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || (uintptr_t)ptr % kAlign) return fail(MUON_E_HIP, "scratch array address %p is not 256-byte aligned", ptr);
+    e = prepare_stage_kernels();
+    if (e == hipSuccess) e = prepare_bf16_kernels();
+    if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute(dynamic LDS)");
+    g_scratch_dev[dev] = ptr;
+  }
+  *dev_ptr = g_scratch_dev[dev];
+  *host = &g_scratch_host[dev];
+  return MUON_OK;
+}
+}  // namespace
+
+int muon_step_scratch(const muon_matrix_desc* descs, int n, const muon_options* opts, float a, float b, float c,
+                      int T, float momentum, int nesterov, float lr, void* hip_stream) {
+  g_err.clear();
+  Options o;
+  int rc = read_options(opts, &o);
+  if (rc) return rc;
+  if (o.zero) return fail(MUON_E_INVAL, "options.zero_momentum is not supported by muon_step_scratch");
+  o.groups = 1;  // one stream: the caller's
+  if (T < 0 || T > o.maxT) return fail(MUON_E_INVAL, "T=%d outside [0, max_T=%d]", T, o.maxT);
+  if (!std::isfinite(a) || !std::isfinite(b) || !std::isfinite(c)) return fail(MUON_E_INVAL, "a, b and c must be finite");
+  if (!std::isfinite(lr)) return fail(MUON_E_INVAL, "lr must be finite");
+  if (!(momentum >= 0.f && momentum <= 1.f)) return fail(MUON_E_INVAL, "momentum %g outside [0, 1]", momentum);
+  rc = validate_all(descs, n, true);
+  if (rc) return rc;
+
+  muon_plan p;  // host state of this call only: no streams, events or pinned memory
+  p.n = n;
+  p.opt = o;
+  p.desc.assign(descs, descs + n);
+  p.geo.resize(n);
+  for (int i = 0; i < n; ++i) p.geo[i] = geometry(descs[i], o.path);
+  p.tab = build_tables(p.geo, o.groups);
+  const size_t need = layout(p.geo, o, p.tab, &p.lay);
+  if (need > kScratchBytes)
+    return fail(MUON_E_WORKSPACE, "this step needs %zu bytes of scratch; muon_step_scratch holds %zu (use muon_init "
+                "with a workspace)", need, kScratchBytes);
+  void* dev_scratch = nullptr;
+  std::vector<char>* host = nullptr;
+  rc = scratch_for_current_device(&dev_scratch, &host);
+  if (rc) return rc;
+  p.ws = (char*)dev_scratch;
+  p.ws_bytes = kScratchBytes;
+  p.hmat.resize(n);
+  for (int i = 0; i < n; ++i) p.hmat[i] = make_devmat(&p, i);
+
+  // Tile tables and the matrix table, staged in this device's pageable host
+  // buffer and copied into the scratch array on the caller's stream.
+  hipStream_t stream = (hipStream_t)hip_stream;
+  std::vector<std::pair<const void*, std::pair<size_t, size_t>>> parts;  // (source, (scratch offset, bytes))
+  for (int grp = 0; grp < kGroups; ++grp)
+    parts.push_back({p.tab.mom[grp].data(), {p.lay.mom_tiles[grp], sizeof(Tile) * p.tab.mom[grp].size()}});
+  for (int grp = 0; grp < kGroups; ++grp)
+    for (int prec = 0; prec < 2; ++prec)
+      for (int k = 0; k < 3; ++k)
+        parts.push_back({p.tab.ns[grp][prec][k].data(),
+                         {p.lay.ns_tiles[grp][prec][k], sizeof(Tile) * p.tab.ns[grp][prec][k].size()}});
+  parts.push_back({p.hmat.data(), {p.lay.slots, sizeof(DevMat) * n}});
+  size_t total = 0;
+  for (auto& q : parts) total += q.second.second;
+  host->resize(std::max<size_t>(total, 16));
+  char* hp = host->data();
+  for (auto& q : parts) {
+    const size_t bytes = q.second.second;
+    if (!bytes) continue;
+    std::memcpy(hp, q.first, bytes);
+    hipError_t e = hipMemcpyAsync(p.ws + q.second.first, hp, bytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(tables into scratch)");
+    hp += bytes;
+  }
+  return enqueue_step(&p, (const DevMat*)(p.ws + p.lay.slots), nullptr, a, b, c, T, momentum, nesterov, lr, stream);
+}

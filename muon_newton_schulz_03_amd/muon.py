@@ -92,6 +92,22 @@ def describe(shapes: Sequence[Tuple[int, int]], path: str = "bf16", x_master_ite
     return d, tiles
 
 
+def step_scratch(weights: Sequence[torch.Tensor], grads: Sequence[torch.Tensor], moms: Sequence[torch.Tensor], *,
+                 a: float = DEFAULT_COEFFS[0], b: float = DEFAULT_COEFFS[1], c: float = DEFAULT_COEFFS[2],
+                 T: int = 5, momentum: float = 0.95, nesterov: bool = True, lr: float = 0.05,
+                 path: str = "bf16", x_master_iters: int = -1, max_T: int = 0,
+                 scales: Optional[Sequence[float]] = None) -> None:
+    """One Muon step over these matrices through muon_step_scratch: no plan and no
+    workspace; the library's static device array holds the working memory, so
+    nothing is allocated.  Enqueued on the current torch stream."""
+    lib = _lib.load()
+    descs = _tensor_descs(weights, grads, moms, None if scales is None else list(scales))
+    opts = _options(path, x_master_iters, False, max_T, 1)
+    stream = torch.cuda.current_stream(weights[0].device).cuda_stream
+    _lib.check(lib.muon_step_scratch(descs, len(weights), ctypes.byref(opts), a, b, c, T, momentum,
+                                     int(bool(nesterov)), lr, ctypes.c_void_p(stream)))
+
+
 class MuonStep:
     """A Muon plan over a fixed list of hidden matrices.
 
