@@ -76,38 +76,53 @@ def read_traffic(kind: str):
     return read_profile_value("hbm_traffic", f"{kind}_hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, budget_s: float = 12.0):
-    """Time the fp64 oracle (as it stands) on a bounded sample: layer 0's six matrices, one step each."""
+def cpu_info():
+    """Logical CPUs this process may use, the CPU model, and the BLAS thread count."""
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        nproc = os.cpu_count()
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"), default=None)
+    except Exception:  # pragma: no cover
+        blas = None
+    return nproc, model, blas
+
+
+def cpu_baseline(wl, reps: int = 3):
+    """Time the fp64 oracle (as it stands) on full steps of the workload: all 72
+    matrices, one Muon step each, `reps` times; the median step is the value."""
     import numpy as np
-    import torch
 
     from muon_newton_schulz_03_amd import inputs
     from oracle import muon_oracle as O
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=os.cpu_count())
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
-    idx = list(range(6))
-    grads = inputs.gradients(WORKLOAD, 0, indices=idx)
-    zeros = [np.zeros(wl.shapes[i]) for i in idx]
-    mz = [np.zeros(wl.shapes[i], np.float32) for i in idx]
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        for k, i in enumerate(idx):
-            O.muon_step(zeros[k], grads[k], mz[k], a=wl.coeffs[0], b=wl.coeffs[1], c=wl.coeffs[2], T=wl.T,
-                        mu=wl.momentum, nesterov=wl.nesterov, lr=wl.lr)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 50:
-            break
-    layers = len(wl.shapes) // 6
-    steps_per_s = reps / (el * layers)
-    return {"value": steps_per_s, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"layer 0 (6 of 72 matrices: 4x768x768, 768x3072, 3072x768), {reps} oracle step(s) "
-                      f"in {el:.1f} s, scaled by 12 layers"}
+    nproc, model, blas = cpu_info()
+    grads = inputs.gradients(WORKLOAD, 0)
+    times = []
+    for _ in range(reps):
+        mz = [np.zeros(s, np.float32) for s in wl.shapes]
+        t0 = time.perf_counter()
+        for i, shape in enumerate(wl.shapes):
+            O.muon_step(np.zeros(shape), grads[i], mz[i], a=wl.coeffs[0], b=wl.coeffs[1], c=wl.coeffs[2],
+                        T=wl.T, mu=wl.momentum, nesterov=wl.nesterov, lr=wl.lr)
+        times.append(time.perf_counter() - t0)
+    med = float(np.median(times))
+    return {"value": 1.0 / med, "unit": "steps/s", "cores": int(blas or nproc), "kind": "oracle",
+            "sample": f"{reps} full steps of all {len(wl.shapes)} matrices (median {med:.2f} s, "
+                      f"min {min(times):.2f} s, max {max(times):.2f} s)",
+            "nproc": nproc, "cpu_model": model, "blas_threads": blas,
+            "seconds_per_step": [round(t, 3) for t in times]}
 
 
 def after_timed_region(args, plan, grads, total, kw, wl, W, M, work, dom):
@@ -189,6 +204,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--repeats", type=int, default=5, help="times the K-step timed region is run (median reported)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the passes after the timed region (one-stream roofline, schedule, graph)")
@@ -261,20 +277,24 @@ def main():
         mk["gbs"] = momentum_bytes(wl.shapes, True) / mk["launches_per_step"] / (mk["ms_per_launch"] * 1e-3) / 1e9
     dom = max(("gram", "poly", "update", "momentum"), key=lambda k: prof_all[k][0])
 
-    # timed region: K steps; HIP events (recorded by the library on this stream)
-    # time the dominant kernel's launches only
+    # timed region: K steps, repeated; HIP events (taken by the library's own
+    # launches on their streams) time the dominant kernel's launches only
     plan.profile(True, kinds=[dom])
     plan.read_profile()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for t in range(args.warmup, total):
-        plan.step(grads=grads[t], **kw)
-    stop.record()
-    torch.cuda.synchronize()
-    ms_total = start.elapsed_time(stop)
+    rep_ms = []
+    for rep in range(args.repeats):
+        torch.cuda.synchronize()
+        start.record()
+        for t in range(args.warmup, total):
+            plan.step(grads=grads[t], **kw)
+        stop.record()
+        torch.cuda.synchronize()
+        rep_ms.append(start.elapsed_time(stop))
     prof = plan.read_profile()
     plan.profile(False)
+    rep_ms_step = sorted(m / args.steps for m in rep_ms)
+    ms_total = sorted(rep_ms)[len(rep_ms) // 2]
 
     extras = {}
     if not args.no_extras:
@@ -285,22 +305,27 @@ def main():
     tflops = work["step"] * steps_per_s / 1e12
     d_ms, d_cnt = prof[dom]
     d_launch_ms = d_ms / d_cnt
+    d_per_step = d_cnt / (args.steps * args.repeats)
     if dom == "momentum":
-        achieved = momentum_bytes(wl.shapes, True) / (d_cnt / args.steps) / (d_launch_ms * 1e-3) / 1e9
+        achieved = momentum_bytes(wl.shapes, True) / d_per_step / (d_launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS}
     else:
-        achieved = wl.T * work[dom] / (d_cnt / args.steps) / (d_launch_ms * 1e-3) / 1e12
+        achieved = wl.T * work[dom] / d_per_step / (d_launch_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS}
     roof["kernel"] = dom
+    roof["scope"] = "per launch of the dominant kernel, averaged over the timed region"
     roof["ms_per_launch"] = d_launch_ms
-    roof["launches_per_step"] = d_cnt / args.steps
+    roof["launches_per_step"] = d_per_step
     roof["traffic"] = read_traffic(dom)
     # share of SIMD cycles with the MFMA unit busy (rocprofv3 counters), when fresh
     roof["mfma_busy"] = read_profile_value("mfma_busy", f"{dom}_mfma_busy")
-    roof["note"] = ("the plan runs two matrix groups on two streams, so each launch covers half the set "
-                    "and shares the GPU with the other group's launches")
+    roof["step_frac"] = tflops / PEAK_BF16_TFLOPS
+    roof["note"] = ("frac is per launch: the plan runs two matrix groups on two streams, so each launch covers "
+                    "half the set and shares the GPU with the other group's launches; step_frac is the whole "
+                    "step's algorithmic rate against the same peak, and roofline_one_stream the kernel's own "
+                    "rate without the overlap")
 
     out = {
         "metric": "Muon steps/s on GPT-2-small hidden set (T=5); % bf16 MFMA peak",
@@ -318,6 +343,11 @@ def main():
         "config": {"workload": "gpt2_small_hidden_72", "matrices": n, "params": wl.params, "T": wl.T,
                    "grad_dtype": "bf16", "weight_dtype": "f32", "momentum": wl.momentum, "nesterov": True,
                    "lr": wl.lr, "coeffs": list(wl.coeffs)},
+        "repeats": {"n": args.repeats, "ms_per_step": [round(m, 4) for m in rep_ms_step],
+                    "median": rep_ms_step[len(rep_ms_step) // 2], "min": rep_ms_step[0], "max": rep_ms_step[-1],
+                    "spread_pct": 100.0 * (rep_ms_step[-1] - rep_ms_step[0]) / rep_ms_step[len(rep_ms_step) // 2],
+                    "note": f"the timed region ({args.steps} steps) run {args.repeats} times; value and "
+                            "ms_per_step are the median run"},
         "tflops_algorithmic": tflops,
         "frac_bf16_peak": tflops / PEAK_BF16_TFLOPS,
         "tflops_dense_model": work["dense_step"] * steps_per_s / 1e12,

@@ -33,3 +33,9 @@ def test_profile_summaries_are_text_with_commands():
         assert name.endswith((".txt", ".md")), name
         text = open(path).read()
         assert "rocprofv3" in text and len(text) < 20000
+
+
+def test_cpu_info_names_the_host():
+    nproc, model, blas = bench.cpu_info()
+    assert nproc >= 1 and isinstance(model, str) and model
+    assert blas is None or blas >= 1
