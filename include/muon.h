@@ -218,9 +218,11 @@ typedef struct muon_plan_info {
                                 4): momentum and norm have n_groups launches per
                                 step, a product kind T * n_groups (times the
                                 precisions present) */
-  int32_t bf16_tile_rows;    /* bf16 products: output tile rows (256); the short side
-                                of such a matrix is padded to a multiple of it */
-  int32_t bf16_tile_cols;    /* bf16 products: output tile columns (128) */
+  int32_t bf16_tile_rows;    /* bf16 polynomial and update products: output tile rows
+                                (256); the short side of such a matrix is padded to a
+                                multiple of it */
+  int32_t bf16_tile_cols;    /* bf16 products: output tile columns (128); the Gram
+                                product takes square tiles of this edge */
 } muon_plan_info;
 
 int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts,

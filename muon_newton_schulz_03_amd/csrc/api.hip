@@ -282,16 +282,18 @@ Tables build_tables(const std::vector<Geometry>& geo, int groups) {
       if (g.f32 != prec || group_of(i) != grp) continue;
       const double K1 = g.np / 128.0, K2 = g.mp / 128.0;
       if (prec == 0) {
-        // bf16: 256 x 128 tiles (row panel a of 256 rows, column panel b of 128);
-        // symmetric products take the tiles reaching the upper triangle at 128
-        // granularity; when b == 2a, rows 128..255 lie below it (half the work)
+        // bf16: the Gram product takes 128 x 128 tiles on or above the diagonal
+        // (a diagonal tile costs a full one: its idle wave keeps pace with the
+        // others through the slab barriers).  The polynomial and the update
+        // take 256 x 128 tiles (row panel a of 256 rows, column panel b of 128);
+        // the polynomial's are those reaching the upper triangle at 128
+        // granularity, b >= 2a, and when b == 2a rows 128..255 lie below it.
         const int tm = g.mp / kTileRowsBf16, tc = g.mp / kTile, tn = g.np / kTile;
+        for (int a = 0; a < tc; ++a)
+          for (int b = a; b < tc; ++b) gram[i].push_back(CostTile{Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0}, K1});
         for (int a = 0; a < tm; ++a)
-          for (int b = 2 * a; b < tc; ++b) {
-            const double halves = b == 2 * a ? 1.0 : 2.0;
-            gram[i].push_back(CostTile{Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0}, halves * K1});
-            poly[i].push_back(CostTile{Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0}, halves * K2});
-          }
+          for (int b = 2 * a; b < tc; ++b)
+            poly[i].push_back(CostTile{Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0}, (b == 2 * a ? 1.0 : 2.0) * K2});
         // update tiles column panel by column panel: the tiles of one X column
         // panel run together and share it in L2
         for (int b = 0; b < tn; ++b)

@@ -9,25 +9,31 @@
 //            weight step W <- W - lr scale O instead of storing X
 //
 // Design (one persistent kernel per product kind):
-//   * output tile 256 rows x 128 columns per 256-thread block, two blocks per
-//     CU; wave w owns rows 128 (w >> 1) .. +127 and columns 64 (w & 1) .. +63
-//     as 4 x 2 v_mfma_f32_32x32x16_bf16 blocks (128 accumulator registers).
-//     Per K step a wave reads 4 + 2 fragments from LDS for 8 MFMAs (64x64
-//     wave tiles read twice as many per MFMA), and a block moves 48 bytes
-//     from L2 per 512 FLOP-clocks of its CU (64 for 128x128 tiles);
+//   * the update's output tile is 256 rows x 128 columns per 256-thread block,
+//     two blocks per CU; wave w owns rows 128 (w >> 1) .. +127 and columns
+//     64 (w & 1) .. +63 as 4 x 2 v_mfma_f32_32x32x16_bf16 blocks (128
+//     accumulator registers).  Per K step a wave reads 4 + 2 fragments from
+//     LDS for 8 MFMAs, and a block moves 48 bytes from L2 per 512 FLOP-clocks
+//     of its CU (64 for 128x128 tiles).  The polynomial takes the same tiles;
+//     the Gram product takes 128 x 128 tiles (wave w: rows 64 (w >> 1),
+//     columns 64 (w & 1), 2 x 2 blocks) for balance: its tiles' K (= n)
+//     differs fourfold within a launch;
 //   * X, its low bytes, A and B are stored in 128-row x 32-column tiles (each
 //     tile contiguous), so a K slab of 32 elements of a 128-row panel is one
 //     contiguous 8 KiB tile: every direct-to-LDS request reads 1 KiB of
 //     contiguous memory (whole cache lines), and every 32 x 32 output block
 //     is 2 KiB of contiguous memory;
-//   * K streams in 32-element slabs through a three-slot LDS ring filled by
-//     direct-to-LDS buffer loads; slab kt + 2 is requested as slab kt
-//     starts, and the ring runs on from one tile into the next, so a tile's
-//     first two slabs are in flight during the previous tile's epilogue;
-//   * A and B are stored in full.  Stages 1 and 2 compute only tiles that
-//     reach the upper triangle (at 128 granularity) and write every element
-//     at (i, j) and at (j, i); diagonal 32-blocks are made exactly symmetric
-//     first.  So every operand is read K-contiguous (ds_read_b128), except X
+//   * K streams in 32-element slabs through an LDS ring filled by
+//     direct-to-LDS buffer loads (three 24 KiB slots for 256-row tiles, five
+//     16 KiB slots for 128-row tiles); slab kt + slots - 1 is
+//     requested as slab kt starts, and the ring runs on from one tile into the
+//     next, so a tile's first slabs are in flight during the previous tile's
+//     epilogue;
+//   * A and B are stored in full.  Stages 1 and 2 compute only the tiles
+//     that reach the upper triangle (at 128 granularity) and write every
+//     element at (i, j) and at (j, i); diagonal 32-blocks are made exactly
+//     symmetric first, and a tile on the diagonal reads its column panel from
+//     the matching half of its row panel.  So every operand is read K-contiguous (ds_read_b128), except X
 //     as the right operand of B X, read with the transposing
 //     ds_read_b64_tr_b16;
 //   * stage 3 adds a X inside the K loop: the X slab of K rows k0 .. k0 + 31
@@ -57,7 +63,27 @@ constexpr int kLds = kLoBase + 2 * kLoBuf;    // 80 KiB: two blocks per CU
 constexpr int kBlock = 32 * 32 * 4;           // one staged 32 x 32 fp32 block per wave
 constexpr int kBlocks = 2;                    // resident blocks per CU
 constexpr uint32_t kOob = 0x80000000u;        // buffer offset past every resource: load 0, store dropped
-constexpr int kDma = 6;                       // ring requests per wave per slab
+constexpr int kDma = 6;                       // ring requests per wave per slab (stage 3)
+
+// Tile shape per stage.  Stages 2 and 3 take 256 x 128 tiles: their K loop
+// moves fewer L2-to-LDS bytes per FLOP than with 128-row tiles.  The Gram
+// product (stage 1) takes 128 x 128 tiles: a tile's K is n, up to four times
+// another's in one launch, and with 256-row tiles the launch waits for its
+// longest tiles; its slots hold two 128-row panels, and the spare LDS buys a
+// deeper ring.
+template <int STAGE>
+struct Shape {
+  static constexpr bool kWide = STAGE != 1;
+  static constexpr int kRows = kWide ? 256 : 128;   // tile rows
+  static constexpr int kMI = kRows / 64;            // 32-row accumulator blocks per wave
+  static constexpr int kSlot = kWide ? 3 * kHalf : 2 * kHalf;
+  static constexpr int kPOff = kWide ? 2 * kHalf : kHalf;  // column panel inside a slot
+  static constexpr int kRing = kWide ? 3 : 5;
+  static constexpr int kAhead = kRing - 1;          // slabs requested ahead
+  static constexpr int kDma = kSlot / 1024 / 4;     // requests per wave per slab
+  static_assert(kWide || kRing * kSlot <= kLds, "ring fits the block's LDS");
+  static_assert(4 * kBlock <= kSlot, "staged epilogue blocks fit one slot");
+};
 
 // Swizzles (16-byte chunk c of row r sits at chunk c ^ swz(r)), each checked
 // in a bank model of 16 lanes per 256-byte cycle for its access patterns.
@@ -157,8 +183,8 @@ struct Ctx {
   uint32_t pblk;            // bytes per 128-row block of P's matrix
   int nk;                   // K slabs
   int i0, j0;               // output origin
-  int psrc;                 // 0: P from its own slab region; 1, 2: from Q half 0, 1
-  int skip1;                // rows 128..255 of the tile have nothing to compute
+  int psrc;                 // 0: P from its own slab region; 1, 2: from Q half 0, 1 (on the diagonal)
+  int skip1;                // 256-row tiles of stage 2: rows 128..255 lie below the diagonal
 };
 
 template <int STAGE, int MODE>
@@ -167,7 +193,7 @@ __device__ __forceinline__ Ctx ctx_of(const StageArgs& args, const Tile& tl) {
   const uint32_t mp = (uint32_t)load_uniform(&m->mp), np = (uint32_t)load_uniform(&m->np);
   const void* xin = ((args.t - 1) & 1) ? load_uniform(&m->xo[1]) : load_uniform(&m->xo[0]);
   Ctx c;
-  c.i0 = tl.ti * kTM;
+  c.i0 = tl.ti * Shape<STAGE>::kRows;
   c.j0 = tl.tj * kTN;
   c.psrc = 0;
   c.skip1 = 0;
@@ -181,10 +207,13 @@ __device__ __forceinline__ Ctx ctx_of(const StageArgs& args, const Tile& tl) {
     c.qoff = (uint32_t)(c.i0 >> 7) * c.qblk;
     c.poff = (uint32_t)(c.j0 >> 7) * c.pblk;
     c.nk = (int)K / kBK;
-    // the column panel is one of the row halves on the tile's diagonal
-    const int rel = tl.tj - 2 * tl.ti;
-    if (rel == 0 || rel == 1) c.psrc = rel + 1;
-    c.skip1 = rel == 0;  // rows 128..255 lie below the diagonal
+    if (Shape<STAGE>::kWide) {  // the column panel is one of the row halves on the tile's diagonal
+      const int rel = tl.tj - 2 * tl.ti;
+      if (rel == 0 || rel == 1) c.psrc = rel + 1;
+      c.skip1 = rel == 0;
+    } else {
+      c.psrc = tl.ti == tl.tj;
+    }
   } else {
     c.q = load_uniform(&m->b);
     c.qbytes = ab;
@@ -204,21 +233,22 @@ __device__ __forceinline__ Ctx ctx_of(const StageArgs& args, const Tile& tl) {
 // parts the tile does not need get empty resources, which move nothing).
 template <int STAGE>
 __device__ __forceinline__ void issue_slab(char* smem, const Ctx& c, int kt, int slot, int w, int lane) {
-  char* s = smem + slot * kSlot;
+  using G = Shape<STAGE>;
+  char* s = smem + slot * G::kSlot;
   const uint32_t kb = (uint32_t)kt * 8192u;
   dma_half(s, make_rsrc(c.q, c.p ? c.qbytes : 0u), c.qoff + kb, w, lane);
-  dma_half(s + kHalf, make_rsrc(c.q, c.p && !c.skip1 ? c.qbytes : 0u), c.qoff + c.qblk + kb, w, lane);
+  if (G::kWide) dma_half(s + kHalf, make_rsrc(c.q, c.p && !c.skip1 ? c.qbytes : 0u), c.qoff + c.qblk + kb, w, lane);
   const rsrc_t p = make_rsrc(c.p, c.p && !c.psrc ? c.pbytes : 0u);
   if (STAGE == 3)
-    dma_xslab(s + 2 * kHalf, p, c.poff + (uint32_t)(kt >> 2) * c.pblk + (uint32_t)(kt & 3) * 2048u, w, lane);
+    dma_xslab(s + G::kPOff, p, c.poff + (uint32_t)(kt >> 2) * c.pblk + (uint32_t)(kt & 3) * 2048u, w, lane);
   else
-    dma_half(s + 2 * kHalf, p, c.poff + kb, w, lane);
+    dma_half(s + G::kPOff, p, c.poff + kb, w, lane);
 }
 
 // Request X's low bytes of slab kt into low-byte buffer `buf` (1 instruction
 // per wave; empty unless the slab's K rows are output rows of the tile).
 __device__ __forceinline__ void issue_lo(char* smem, const Ctx& c, int kt, int buf, int w, int lane) {
-  const bool need = c.p && kt * kBK >= c.i0 && kt * kBK < c.i0 + kTM;
+  const bool need = c.p && kt * kBK >= c.i0 && kt * kBK < c.i0 + kTM;  // stage 3 only
   dma_lo(smem + kLoBase + buf * kLoBuf, make_rsrc(c.xlo, need ? (c.pbytes >> 1) : 0u),
          (c.poff >> 1) + (uint32_t)(kt >> 2) * (c.pblk >> 1) + (uint32_t)(kt & 3) * 1024u, w, lane);
 }
@@ -241,14 +271,14 @@ __device__ __forceinline__ FragOff frag_off(int lane) {
 // is the P fragment (MFMA row <-> output column), operand B the Q fragment,
 // so lane l holds output row 32 mi + l % 32 and 4 consecutive output columns
 // per group of 4 accumulator registers.
-template <bool PX>
-__device__ __forceinline__ void mma_slab(f32x16 (&acc)[4][2], const char* qh, const char* p, int wn, int lane,
+template <bool PX, int MI>
+__device__ __forceinline__ void mma_slab(f32x16 (&acc)[MI][2], const char* qh, const char* p, int wn, int lane,
                                          const FragOff& fo) {
-  u32x4 qf[2][4], pf[2][2];
+  u32x4 qf[2][MI], pf[2][2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) qf[ks][mi] = *(const u32x4*)(qh + mi * 2048 + fo.row + fo.ch[ks]);
+    for (int mi = 0; mi < MI; ++mi) qf[ks][mi] = *(const u32x4*)(qh + mi * 2048 + fo.row + fo.ch[ks]);
     if (PX) {
       frags_xs(pf[ks], p, 64 * wn, lane, ks);
     } else {
@@ -259,7 +289,7 @@ __device__ __forceinline__ void mma_slab(f32x16 (&acc)[4][2], const char* qh, co
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int nj = 0; nj < 2; ++nj)
         acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pf[ks][nj]),
@@ -409,8 +439,8 @@ __device__ __forceinline__ void wait_vm(int n) {
   else MUON_WAIT_VMCNT(0);
 }
 
-// Epilogue of one wave over its eight 32 x 32 accumulator blocks (b = 2 mi +
-// nj).  Inputs per block (A of stage 2 at the direct positions, W of the
+// Epilogue of one wave over its 32 x 32 accumulator blocks (b = 2 mi + nj:
+// eight in stage 3, four in stages 1 and 2).  Inputs per block (A of stage 2 at the direct positions, W of the
 // weight step) are requested kDepth blocks ahead.
 template <int STAGE, int MODE>
 struct Epi {
@@ -419,6 +449,8 @@ struct Epi {
   static constexpr bool kLoOut = kUpd && !kLastIt && (MODE & kWriteLo);
   static constexpr int kDepth = STAGE == 2 ? 3 : (kLastIt ? 2 : 0);
   static constexpr int kInSlots = kDepth > 0 ? kDepth : 1;
+  static constexpr int kMI = Shape<STAGE>::kMI;
+  static constexpr int kNB = 2 * kMI;  // the wave's 32 x 32 blocks
   struct In {
     u32x4 v[4];  // stage 2: A of row passes 0, 1 (bf16); weight step: W as fp32 bit patterns
   };
@@ -436,7 +468,7 @@ struct Epi {
 
   __device__ __forceinline__ Epi(const StageArgs& args, const DevMat* m, const Ctx& c, int wm, int wn, int lane_)
       : lane(lane_) {
-    R0 = c.i0 + 128 * wm;
+    R0 = c.i0 + (Shape<STAGE>::kRows / 2) * wm;
     C0 = c.j0 + 64 * wn;
     sub = R0 >> 7;
     tj = c.j0 >> 7;
@@ -479,7 +511,7 @@ struct Epi {
   enum { kOff = 0, kDiag = 1, kLower = 2 };
   __device__ __forceinline__ int kind(int b) const {
     if (sub < tj) return kOff;
-    const int dr = 32 * (b >> 1), dc = (C0 & 127) + 32 * (b & 1);  // offsets in the diagonal subtile
+    const int dr = (R0 & 127) + 32 * (b >> 1), dc = (C0 & 127) + 32 * (b & 1);  // offsets in the diagonal subtile
     return dr < dc ? kOff : dr == dc ? kDiag : kLower;
   }
 
@@ -603,12 +635,12 @@ struct Epi {
   // slabs).  Block b + kDepth's inputs are requested once block b has been
   // processed (its input registers are then free).  Returns the instructions
   // the epilogue itself issued.
-  __device__ __forceinline__ int run(const f32x16 (&acc)[4][2], const Stage& st, In (&in)[kInSlots],
+  __device__ __forceinline__ int run(const f32x16 (&acc)[kMI][2], const Stage& st, In (&in)[kInSlots],
                                      int vm_pre) const {
     const int lpb = loads_per_block(), spb = stores_per_block();
     int issued = 0;
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
+    for (int b = 0; b < kNB; ++b) {
       st.put(acc[b >> 1][b & 1], lane);
       if (kDepth > 0 && lpb > 0) {
         // instructions issued after block b's request, which may stay in flight
@@ -616,14 +648,14 @@ struct Epi {
         if (b < kDepth) {
           after = (kDepth - 1 - b) * lpb + vm_pre + issued;
         } else {
-          const int last_req = b + kDepth - 1 < 8 ? b + kDepth - 1 : 7;
+          const int last_req = b + kDepth - 1 < kNB ? b + kDepth - 1 : kNB - 1;
           after = (kDepth - 1) * spb + (last_req - b) * lpb;
         }
         wait_vm(after);
       }
       process(b, st, in[b % kInSlots]);
       issued += spb;
-      if (kDepth > 0 && lpb > 0 && b + kDepth < 8) {
+      if (kDepth > 0 && lpb > 0 && b + kDepth < kNB) {
         load(b + kDepth, in[(b + kDepth) % kInSlots]);
         issued += lpb;
       }
@@ -638,8 +670,11 @@ struct Epi {
 template <int STAGE, int MODE>
 __global__ __launch_bounds__(kThreads, kBlocks) void ns_bf16_kernel(StageArgs args) {
   using E = Epi<STAGE, MODE>;
+  using G = Shape<STAGE>;
   constexpr bool kLoIn = STAGE == 3 && (MODE & kHiLo);
   constexpr int kDepth = E::kDepth;
+  constexpr int kAhead = G::kAhead;
+  constexpr int kD = G::kDma;  // requests per wave per slab
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -654,10 +689,10 @@ __global__ __launch_bounds__(kThreads, kBlocks) void ns_bf16_kernel(StageArgs ar
   Tile tl = tile_of(raw);
   Ctx c = ctx_of<STAGE, MODE>(args, tl);
   if (kLoIn) issue_lo(smem, c, 0, 0, w, lane);
-  issue_slab<STAGE>(smem, c, 0, 0, w, lane);
-  issue_slab<STAGE>(smem, c, 1, 1, w, lane);
-  int g = 0;     // slabs consumed by this block so far (ring slot g % 3, low-byte buffer g % 2)
-  int pend = 0;  // the previous epilogue's instructions, issued after this tile's first two slabs
+#pragma unroll
+  for (int d = 0; d < kAhead; ++d) issue_slab<STAGE>(smem, c, d, d, w, lane);
+  int g = 0;     // slabs consumed by this block so far (ring slot g % kRing, low-byte buffer g % 2)
+  int pend = 0;  // the previous epilogue's instructions, issued after this tile's first kAhead slabs
   for (;;) {
     // the block's next tile, for the requests that run ahead into it
     uint64_t rawn = 0;
@@ -669,48 +704,59 @@ __global__ __launch_bounds__(kThreads, kBlocks) void ns_bf16_kernel(StageArgs ar
       cn = ctx_of<STAGE, MODE>(args, tn);
     else
       cn.p = nullptr;  // empty requests keep the wait counts static
-    // waves whose rows lie wholly below the diagonal (stages 1 and 2) only move data
-    const bool idle = STAGE != 3 && (wm == 1 && c.skip1);
-    const int psrc = c.psrc;
-    const int R0 = c.i0 + 128 * wm;
+    // on a diagonal tile of stages 1 and 2, waves whose rows lie wholly below
+    // the diagonal only move data
+    const bool idle = STAGE != 3 && (G::kWide ? wm == 1 && c.skip1 : c.psrc && wm == 1 && wn == 0);
+    const int R0 = c.i0 + (G::kRows / 2) * wm;
     float alpha = args.a;
     if (STAGE == 3 && args.t == 1) alpha *= load_uniform(load_uniform(&args.mats[tl.mat].sc));
     typename E::In in[E::kInSlots];
 
-    f32x16 acc[4][2];
+    f32x16 acc[G::kMI][2];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < G::kMI; ++mi)
 #pragma unroll
       for (int nj = 0; nj < 2; ++nj)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[mi][nj][v] = 0.f;
 
-    const int nk = c.nk;
-    int vm_pre = 0;  // instructions issued after the epilogue's early input requests
+    const int nk = c.nk;  // >= 2 kAhead: K is a multiple of 256
+    // stage 2: the epilogue's first A requests, made as slab nk - kAhead starts
+    const int early = STAGE == 2 && !idle ? kDepth * 2 : 0;
+    int vm_pre = 0;  // instructions issued after those requests
     for (int kt = 0; kt < nk; ++kt) {
-      // this wave's part of slab kt (and its low bytes) has landed: only slab
-      // kt + 1's requests may still be in flight, plus, at the first slabs of
-      // a tile, the previous epilogue's stores
-      if (kt == 0 || (kt == 1 && !kLoIn))
-        wait_vm(kDma + pend);
-      else
-        MUON_WAIT_VMCNT(kDma);
+      // this wave's part of slab kt (and its low bytes) has landed: only the
+      // slabs requested after it may still be in flight, plus, at the first
+      // slabs of a tile, the previous epilogue's instructions, and at the last
+      // slabs of stage 2, the early A requests
+      if (STAGE == 3) {
+        if (kt == 0 || (kt == 1 && !kLoIn))
+          wait_vm(kD + pend);
+        else
+          MUON_WAIT_VMCNT(kD);
+      } else if (kt < kAhead) {
+        wait_vm((kAhead - 1) * kD + pend);
+      } else if (STAGE == 2 && kt > nk - kAhead) {
+        wait_vm((kAhead - 1) * kD + early);
+      } else {
+        MUON_WAIT_VMCNT((kAhead - 1) * kD);
+      }
       MUON_LDS_BARRIER();  // every wave's part has landed; slab kt - 1's slot is free
       if (kLoIn) issue_lo(smem, kt + 1 < nk ? c : cn, kt + 1 < nk ? kt + 1 : kt + 1 - nk, (g + 1) & 1, w, lane);
-      if (STAGE == 2 && kt == nk - 2 && !idle) {  // the epilogue's first inputs
+      if (STAGE == 2 && kt == nk - kAhead && !idle) {  // the epilogue's first inputs
         const E ep(args, args.mats + tl.mat, c, wm, wn, lane);
 #pragma unroll
         for (int b = 0; b < kDepth; ++b) ep.load(b, in[b % E::kInSlots]);
       }
-      const int slot = (g + 2) % kRing;
-      if (kt + 2 < nk)
-        issue_slab<STAGE>(smem, c, kt + 2, slot, w, lane);
+      const int slot = (g + kAhead) % G::kRing;
+      if (kt + kAhead < nk)
+        issue_slab<STAGE>(smem, c, kt + kAhead, slot, w, lane);
       else
-        issue_slab<STAGE>(smem, cn, kt + 2 - nk, slot, w, lane);
-      if (STAGE == 2 && kt >= nk - 2) vm_pre += kDma;
-      const char* s = smem + (g % kRing) * kSlot;
+        issue_slab<STAGE>(smem, cn, kt + kAhead - nk, slot, w, lane);
+      if (STAGE == 2 && kt >= nk - kAhead) vm_pre += kD;
+      const char* s = smem + (g % G::kRing) * G::kSlot;
       if (!idle) {
-        const char* p = psrc ? s + (psrc - 1) * kHalf : s + 2 * kHalf;
+        const char* p = c.psrc ? s + (c.psrc - 1) * kHalf : s + G::kPOff;
         if (STAGE == 3) {
           const int rel = kt * kBK - R0;  // this slab's K rows are output rows of the wave
           if (rel >= 0 && rel < 128) {
@@ -718,12 +764,14 @@ __global__ __launch_bounds__(kThreads, kBlocks) void ns_bf16_kernel(StageArgs ar
             switch (rel >> 5) {
               case 0: fold_x<kLoIn>(acc[0], p, lo, wn, lane, alpha); break;
               case 1: fold_x<kLoIn>(acc[1], p, lo, wn, lane, alpha); break;
-              case 2: fold_x<kLoIn>(acc[2], p, lo, wn, lane, alpha); break;
-              default: fold_x<kLoIn>(acc[3], p, lo, wn, lane, alpha); break;
+              case 2: fold_x<kLoIn>(acc[2 % G::kMI], p, lo, wn, lane, alpha); break;
+              default: fold_x<kLoIn>(acc[3 % G::kMI], p, lo, wn, lane, alpha); break;
             }
           }
+          mma_slab<true, G::kMI>(acc, s + wm * kHalf, p, wn, lane, fo);
+        } else {
+          mma_slab<false, G::kMI>(acc, s + wm * (G::kWide ? kHalf : kHalf / 2), p, wn, lane, fo);
         }
-        mma_slab<STAGE == 3>(acc, s + wm * kHalf, p, wn, lane, fo);
       }
       ++g;
     }
@@ -733,16 +781,16 @@ __global__ __launch_bounds__(kThreads, kBlocks) void ns_bf16_kernel(StageArgs ar
     pend = 0;
     if (!idle) {
       const E ep(args, args.mats + tl.mat, c, wm, wn, lane);
-      int early = 0;  // requests made after the next tile's first slabs, before run()
+      int early_w = 0;  // requests made after the next tile's first slabs, before run()
       if (E::kLastIt) {  // the weight step requests its first W blocks here (registers are short in the loop)
 #pragma unroll
         for (int b = 0; b < kDepth; ++b) ep.load(b, in[b % E::kInSlots]);
         vm_pre = 0;
-        early = kDepth * ep.loads_per_block();
+        early_w = kDepth * ep.loads_per_block();
       }
       Stage st;
-      st.base = smem + ((g + kRing - 1) % kRing) * kSlot + w * kBlock;
-      pend = early + ep.run(acc, st, in, vm_pre);
+      st.base = smem + ((g + G::kRing - 1) % G::kRing) * G::kSlot + w * kBlock;
+      pend = early_w + ep.run(acc, st, in, vm_pre);
     }
     if (!more) break;
     q = qn;

@@ -75,10 +75,11 @@ def test_workspace_size_model(lib):
 
 
 def expected_tiles(shapes, kind, path="bf16"):
-    """Tiles of one launch kind: fp32 products (short side < 64, or the fp32 path)
-    take 128 x 128 tiles over the upper triangle (A, B) or the whole X; bf16
-    products take 256 x 128 tiles (256-row panel a, 128-column panel b), for A
-    and B those with b >= 2a (they reach the upper triangle)."""
+    """Tiles of one launch kind.  fp32 products (short side < 64, or the fp32 path):
+    128 x 128 tiles over the upper triangle (A, B) or the whole X.  bf16 products:
+    the Gram product takes 128 x 128 tiles on or above the diagonal; the polynomial
+    and the update take 256 x 128 tiles (256-row panel a, 128-column panel b), the
+    polynomial's with b >= 2a (they reach the upper triangle)."""
     expect = set()
     for i, (r, c) in enumerate(shapes):
         m, n = min(r, c), max(r, c)
@@ -88,7 +89,7 @@ def expected_tiles(shapes, kind, path="bf16"):
             expect |= {(i, a, b) for a in range(mp // 64) for b in range(np_ // 64)}
         elif f32 and kind == _lib.KIND_UPDATE:
             expect |= {(i, a, b) for a in range(mp // 128) for b in range(np_ // 128)}
-        elif f32:
+        elif f32 or kind == _lib.KIND_GRAM:
             expect |= {(i, a, b) for a in range(mp // 128) for b in range(a, mp // 128)}
         elif kind == _lib.KIND_UPDATE:
             expect |= {(i, a, b) for a in range(mp // 256) for b in range(np_ // 128)}
@@ -112,13 +113,15 @@ def test_tile_lists_cover_each_tile_once(shapes, groups):
 
 
 def tile_cost(shapes, kind, tile):
-    """Work of one bf16 tile in 128 x 128 x 128 units: K / 128 per 128 x 128 half,
-    and a symmetric-product tile with b == 2a computes only its upper half."""
+    """Host cost of one bf16 tile in 32-element K slabs: a Gram tile (128 x 128)
+    costs its K; a polynomial tile (256 x 128) with b == 2a computes only its upper
+    half and counts half."""
     mat, a, b = tile
     r, c = shapes[mat]
-    k = max(r, c) if kind == _lib.KIND_GRAM else min(r, c)
-    halves = 1 if kind != _lib.KIND_UPDATE and b == 2 * a else 2
-    return halves * k // 128
+    if kind == _lib.KIND_GRAM:
+        return max(r, c) // 32
+    k = min(r, c) // 32
+    return k if kind == _lib.KIND_POLY and b == 2 * a else 2 * k
 
 
 def test_block_loads_are_balanced():
