@@ -159,14 +159,16 @@ int muon_step(muon_plan* plan, const muon_matrix_desc* descs, int n, float a, fl
 int muon_step_schedule(muon_plan* plan, const muon_matrix_desc* descs, int n, const float* coeffs, int T,
                        float momentum, int nesterov, float lr, void* hip_stream);
 
-/* For callers that cannot allocate device memory (code under stream capture,
- * tight serving loops, harnesses that forbid hipMalloc): one muon_step over
+/* For callers that cannot allocate device memory (tight serving loops,
+ * harnesses that forbid hipMalloc): one muon_step over
  * the n descriptors without a plan or a workspace.  The working memory (X
  * copies, A, B, partial sums, tables) is a static device array of 64 MiB
  * (MUON_SCRATCH_BYTES) that the library holds on every GPU it runs on until
  * the process ends; the call allocates nothing.  It plans on the host each
  * time, copies the tables into that array from pageable host memory on
  * hip_stream and enqueues the step there (groups is ignored: one stream).
+ * That copy is not meant for stream capture: capture the planned muon_step
+ * instead.
  * Arguments are those of muon_init (opts: path, x_master_iters and max_T;
  * zero_momentum must be 0) and muon_step; the stream must belong to the
  * current device.  A set whose working memory exceeds the array fails with
