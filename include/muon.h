@@ -166,7 +166,8 @@ int muon_step_schedule(muon_plan* plan, const muon_matrix_desc* descs, int n, co
  * (MUON_SCRATCH_BYTES) that the library holds on every GPU it runs on until
  * the process ends; the call allocates nothing.  It plans on the host each
  * time, copies the tables into that array from pageable host memory on
- * hip_stream and enqueues the step there (groups is ignored: one stream).
+ * hip_stream (a later call first waits for that copy to have run) and
+ * enqueues the step there (groups is ignored: one stream).
  * That copy is not meant for stream capture: capture the planned muon_step
  * instead.
  * Arguments are those of muon_init (opts: path, x_master_iters and max_T;

@@ -945,10 +945,13 @@ namespace {
 std::mutex g_scratch_mu;
 void* g_scratch_dev[kMaxDevices] = {};      // device address of `scratch`, per device
 std::vector<char> g_scratch_host[kMaxDevices];  // pageable staging of the tables, per device
+hipEvent_t g_scratch_ev[kMaxDevices] = {};  // recorded after the last table copy out of that staging
+bool g_scratch_ev_used[kMaxDevices] = {};
 
 // Device address of the current device's scratch array (taken on the first
-// call on that device, with the device current) and its host staging buffer.
-int scratch_for_current_device(void** dev_ptr, std::vector<char>** host) {
+// call on that device, with the device current), its host staging buffer and
+// the event that guards the buffer's reuse.
+int scratch_for_current_device(void** dev_ptr, std::vector<char>** host, int* dev_out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -962,10 +965,13 @@ int scratch_for_current_device(void** dev_ptr, std::vector<char>** host) {
     e = prepare_stage_kernels();
     if (e == hipSuccess) e = prepare_bf16_kernels();
     if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute(dynamic LDS)");
+    e = hipEventCreateWithFlags(&g_scratch_ev[dev], hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate(scratch tables)");
     g_scratch_dev[dev] = ptr;
   }
   *dev_ptr = g_scratch_dev[dev];
   *host = &g_scratch_host[dev];
+  *dev_out = dev;
   return MUON_OK;
 }
 }  // namespace
@@ -998,8 +1004,14 @@ int muon_step_scratch(const muon_matrix_desc* descs, int n, const muon_options* 
                 "with a workspace)", need, kScratchBytes);
   void* dev_scratch = nullptr;
   std::vector<char>* host = nullptr;
-  rc = scratch_for_current_device(&dev_scratch, &host);
+  int dev = 0;
+  rc = scratch_for_current_device(&dev_scratch, &host, &dev);
   if (rc) return rc;
+  // the previous call's table copies must have read the staging buffer
+  if (g_scratch_ev_used[dev]) {
+    hipError_t e = hipEventSynchronize(g_scratch_ev[dev]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(scratch tables)");
+  }
   p.ws = (char*)dev_scratch;
   p.ws_bytes = kScratchBytes;
   p.hmat.resize(n);
@@ -1029,5 +1041,8 @@ int muon_step_scratch(const muon_matrix_desc* descs, int n, const muon_options* 
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(tables into scratch)");
     hp += bytes;
   }
+  hipError_t e = hipEventRecord(g_scratch_ev[dev], stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(scratch tables)");
+  g_scratch_ev_used[dev] = true;
   return enqueue_step(&p, (const DevMat*)(p.ws + p.lay.slots), nullptr, a, b, c, T, momentum, nesterov, lr, stream);
 }

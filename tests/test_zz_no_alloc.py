@@ -66,3 +66,20 @@ def test_scratch_step_refuses_sets_beyond_its_array():
     assert err.value.code == MUON_E_WORKSPACE
     torch.cuda.synchronize()
     assert all(torch.equal(w, b) for w, b in zip(W, before))
+
+
+def test_scratch_steps_back_to_back():
+    """Two calls enqueued without a host synchronisation in between (the second
+    smaller): each must still read its own tables."""
+    dev = "cuda:0"
+    first, second = [(256, 384), (768, 768), (384, 256)], [(130, 130)]
+    sets = [tensors(first, 400, dev), tensors(second, 410, dev)]
+    refs = [[[t.clone() for t in part] for part in s] for s in sets]
+    for W, G, M in refs:
+        planned_step(W, G, M, "bf16")
+    for W, G, M in sets:
+        step_scratch(W, G, M, **KW)
+    torch.cuda.synchronize()
+    for (W, _, M), (Wr, _, Mr) in zip(sets, refs):
+        for i in range(len(W)):
+            assert torch.equal(W[i], Wr[i]) and torch.equal(M[i], Mr[i]), i
