@@ -1,4 +1,4 @@
-// gfx950 (CDNA4) bf16 Newton-Schulz products of the Muon step on 256x128 tiles.
+// gfx950 (CDNA4) bf16 Newton-Schulz products of the Muon step.
 //
 // The iteration (overview page "The NanoGPT speedrun", paragraph "Six records
 // account for most of the speedup", record #3: the update is driven towards
@@ -33,9 +33,9 @@
 //     that reach the upper triangle (at 128 granularity) and write every
 //     element at (i, j) and at (j, i); diagonal 32-blocks are made exactly
 //     symmetric first, and a tile on the diagonal reads its column panel from
-//     the matching half of its row panel.  So every operand is read K-contiguous (ds_read_b128), except X
-//     as the right operand of B X, read with the transposing
-//     ds_read_b64_tr_b16;
+//     the matching half of its row panel.  So every operand is read
+//     K-contiguous (ds_read_b128), except X as the right operand of B X, read
+//     with the transposing ds_read_b64_tr_b16;
 //   * stage 3 adds a X inside the K loop: the X slab of K rows k0 .. k0 + 31
 //     holds X at exactly the output rows k0 .. k0 + 31 of the tile's columns,
 //     so the wave owning those rows reads them there (with X's low bytes,
@@ -51,7 +51,7 @@
 namespace muon {
 namespace {
 
-constexpr int kTM = 256;                      // tile rows (Q operand's panel)
+constexpr int kTM = 256;                      // update tile rows (Q operand's panel); see Shape
 constexpr int kTN = 128;                      // tile columns (P operand's panel)
 constexpr int kBK = 32;                       // K elements per slab
 constexpr int kHalf = 128 * 2 * kBK;          // one 128-row half slab: 8 KiB
