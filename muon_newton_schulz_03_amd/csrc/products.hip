@@ -720,7 +720,9 @@ __global__ __launch_bounds__(kThreads, kBlocks) void ns_bf16_kernel(StageArgs ar
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[mi][nj][v] = 0.f;
 
-    const int nk = c.nk;  // >= 2 kAhead: K is a multiple of 256
+    // K slabs: at least kAhead (Gram: K = np >= 128, four slabs); stage 2 has
+    // K = mp >= 256, so its first and last kAhead slabs never overlap
+    const int nk = c.nk;
     // stage 2: the epilogue's first A requests, made as slab nk - kAhead starts
     const int early = STAGE == 2 && !idle ? kDepth * 2 : 0;
     int vm_pre = 0;  // instructions issued after those requests
