@@ -29,7 +29,7 @@
  * distance from hi to X in the integer order of fp32 bit patterns, in units
  * of 256, rounded (about 16 significant bits, relative error <= 2^-15), and as
  * the bf16 copy alone afterwards.  Matrices whose short side is
- * below 64 take the fp32 arithmetic even on this path: their A*A and B*X
+ * below 128 take the fp32 arithmetic even on this path: their A*A and B*X
  * contractions are too short for bf16 rounding errors to average out.
  * MUON_PATH_F32: everything fp32.
  *

@@ -21,10 +21,11 @@ constexpr int kXcds = 8;       // MI355X: 8 XCDs, blocks dispatched round-robin
 constexpr uint16_t kNullMat = 0xFFFF;  // tile-table filler: the block exits
 constexpr double kEps = 1e-7;
 // On the bf16 path, matrices whose short side is below this run the fp32
-// arithmetic: with so few terms in the A*A and B*X contractions the bf16
-// operand rounding does not average out (4x8 inputs reach 2-5e-2 relative
-// error in bf16), while their cost is negligible.
-constexpr int kMinBf16Side = 64;
+// arithmetic: with few terms in the A*A and B*X contractions the bf16 operand
+// rounding averages out less (4x8 inputs reach 2-5e-2 relative error in bf16,
+// short sides of 64 up to 1.8e-2 on MI355X, 128 and more at most 1.4e-2),
+// while their cost is negligible.
+constexpr int kMinBf16Side = 128;
 
 // One matrix, as the kernels see it.
 struct DevMat {

@@ -75,7 +75,7 @@ def test_workspace_size_model(lib):
 
 
 def expected_tiles(shapes, kind, path="bf16"):
-    """Tiles of one launch kind.  fp32 products (short side < 64, or the fp32 path):
+    """Tiles of one launch kind.  fp32 products (short side < 128, or the fp32 path):
     128 x 128 tiles over the upper triangle (A, B) or the whole X.  bf16 products:
     the Gram product takes 128 x 128 tiles on or above the diagonal; the polynomial
     and the update take 256 x 128 tiles (256-row panel a, 128-column panel b), the
@@ -83,7 +83,7 @@ def expected_tiles(shapes, kind, path="bf16"):
     expect = set()
     for i, (r, c) in enumerate(shapes):
         m, n = min(r, c), max(r, c)
-        f32 = path == "f32" or m < 64
+        f32 = path == "f32" or m < 128
         mp, np_ = -(-m // (128 if f32 else 256)) * (128 if f32 else 256), -(-n // 128) * 128
         if kind == _lib.KIND_MOMENTUM:
             expect |= {(i, a, b) for a in range(mp // 64) for b in range(np_ // 64)}
@@ -175,8 +175,8 @@ def test_xcd_runs_are_balanced():
 
 
 def test_short_matrices_take_fp32_products():
-    d, _ = describe([(4, 8), (63, 1000), (64, 64), (768, 768), (3000, 40)])
-    assert d["n_f32_matrices"] == 3
+    d, _ = describe([(4, 8), (127, 1000), (64, 64), (128, 128), (768, 768), (3000, 40)])
+    assert d["n_f32_matrices"] == 4
     d, _ = describe([(4, 8), (768, 768)], path="f32")
     assert d["n_f32_matrices"] == 2
     # each precision has its own launch: the lists hold both sets of tiles

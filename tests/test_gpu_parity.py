@@ -52,6 +52,24 @@ def test_ragged_shapes(path):
     say(f"  worst rel err {worst:.3e}")
 
 
+def test_many_small_matrices_share_blocks():
+    """600 small matrices and two large ones, so that blocks run several tiles
+    of different K back to back and the ring's requests run ahead across tile
+    boundaries; every matrix is compared.  Sides run from 64 to 200: those
+    with a short side of 128 or more take the bf16 products (128 x 128 gives
+    the Gram product 4 K slabs, the least the ring allows), the others the
+    fp32 products in the same step."""
+    say("[gpu] many small matrices")
+    rng = np.random.default_rng(7)
+    sides = [64, 100, 128, 128, 160, 200]
+    shapes = [(int(rng.choice(sides)), int(rng.choice(sides))) for _ in range(600)] + [(768, 3072), (256, 1024)]
+    steps = [[inputs.custom_gradient(r, c, 1300 + 10 * t + i, std=0.02) for i, (r, c) in enumerate(shapes)]
+             for t in range(2)]
+    gpu = run_gpu(shapes, steps, path="bf16", lr=0.5)
+    worst = compare_run(shapes, steps, gpu, path="bf16", lr=0.5, mu=0.95, nesterov=True)
+    say(f"  worst rel err {worst:.3e} over {len(shapes)} matrices")
+
+
 def test_single768_fp32():
     say("[gpu] single768 fp32 path")
     wl = inputs.workload("single768")
