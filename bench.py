@@ -125,9 +125,10 @@ def cpu_baseline(wl, reps: int = 3):
             "seconds_per_step": [round(t, 3) for t in times]}
 
 
-def after_timed_region(args, plan, grads, total, kw, wl, W, M, work, dom):
-    """Measurements after the timed region: the dominant kernel in a one-stream plan,
-    a per-iteration coefficient schedule, and the step replayed from a HIP graph."""
+def after_timed_region(args, plan, grads, total, kw, wl, W, M, work, dom, fused):
+    """Measurements after the timed region: the dominant kernel in a one-stream plan
+    (staged plans), a per-iteration coefficient schedule, and the step replayed
+    from a HIP graph."""
     import torch
 
     from muon_newton_schulz_03_amd import MuonStep
@@ -166,6 +167,15 @@ def after_timed_region(args, plan, grads, total, kw, wl, W, M, work, dom):
     graph_ms = ev0.elapsed_time(ev1) / graph_steps
     del graph
 
+    out = {
+        "schedule": {"coeffs": [list(t) for t in sched], "ms_per_step": sched_ms, "steps_per_s": 1000.0 / sched_ms,
+                     "note": f"muon_step_schedule, {sched_steps} steps after the timed region"},
+        "graph": {"ms_per_step": graph_ms, "steps_per_s": 1000.0 / graph_ms,
+                  "note": f"one step captured in a HIP graph, {graph_steps} replays after the timed region"},
+    }
+    if fused:  # the fused launch already runs alone on one stream
+        return out
+
     # The same kernel without the overlap: a one-stream plan, outside the timed region.
     plan1 = MuonStep(W, grads[0], M, x_master_iters=args.x_master_iters, groups=1)
     for t in range(2):
@@ -190,13 +200,8 @@ def after_timed_region(args, plan, grads, total, kw, wl, W, M, work, dom):
                 "frac": one_ach / one_peak, "kernel": dom, "ms_per_launch": one_ms,
                 "note": f"one-stream plan (groups=1), {one_steps} steps after the timed region"}
 
-    return {
-        "roofline_one_stream": roof_one,
-        "schedule": {"coeffs": [list(t) for t in sched], "ms_per_step": sched_ms, "steps_per_s": 1000.0 / sched_ms,
-                     "note": f"muon_step_schedule, {sched_steps} steps after the timed region"},
-        "graph": {"ms_per_step": graph_ms, "steps_per_s": 1000.0 / graph_ms,
-                  "note": f"one step captured in a HIP graph, {graph_steps} replays after the timed region"},
-    }
+    out["roofline_one_stream"] = roof_one
+    return out
 
 
 def main():
@@ -209,6 +214,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the passes after the timed region (one-stream roofline, schedule, graph)")
     ap.add_argument("--x-master-iters", type=int, default=-1)
+    ap.add_argument("--plan", choices=("staged", "fused"), default="staged",
+                    help="staged: three launches per iteration on two streams; fused: one persistent launch "
+                         "runs every product of the step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 256 MiB device copy first (counter calibration)")
     ap.add_argument("--calibrate-mfma", action="store_true",
@@ -247,7 +255,8 @@ def main():
             gc = ga @ gb
         torch.cuda.synchronize()
         del ga, gb, gc
-    plan = MuonStep(W, grads[0], M, x_master_iters=args.x_master_iters)
+    fused = args.plan == "fused"
+    plan = MuonStep(W, grads[0], M, x_master_iters=args.x_master_iters, fused=fused)
     kw = dict(a=wl.coeffs[0], b=wl.coeffs[1], c=wl.coeffs[2], T=wl.T, momentum=wl.momentum,
               nesterov=wl.nesterov, lr=wl.lr)
     for t in range(args.warmup):
@@ -272,10 +281,12 @@ def main():
         per_kind[k] = {"ms_per_launch": ms / cnt, "launches_per_step": cnt / prof_steps}
         if k in ("gram", "poly", "update"):
             per_kind[k]["tflops"] = wl.T * work[k] / (cnt / prof_steps) / (ms / cnt * 1e-3) / 1e12
+        if k == "fused":
+            per_kind[k]["tflops"] = work["step"] / (cnt / prof_steps) / (ms / cnt * 1e-3) / 1e12
     if "momentum" in per_kind:
         mk = per_kind["momentum"]
         mk["gbs"] = momentum_bytes(wl.shapes, True) / mk["launches_per_step"] / (mk["ms_per_launch"] * 1e-3) / 1e9
-    dom = max(("gram", "poly", "update", "momentum"), key=lambda k: prof_all[k][0])
+    dom = max(("gram", "poly", "update", "momentum", "fused"), key=lambda k: prof_all[k][0])
 
     # timed region: K steps, repeated.  HIP events taken by the library's own
     # launches (on the streams they run on) time the dominant kernel's launches
@@ -307,7 +318,7 @@ def main():
 
     extras = {}
     if not args.no_extras:
-        extras = after_timed_region(args, plan, grads, total, kw, wl, W, M, work, dom)
+        extras = after_timed_region(args, plan, grads, total, kw, wl, W, M, work, dom, fused)
     plan.close()
     ms_step = ms_total / args.steps
     steps_per_s = 1000.0 / ms_step
@@ -319,6 +330,10 @@ def main():
         achieved = momentum_bytes(wl.shapes, True) / d_per_step / (d_launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS}
+    elif dom == "fused":
+        achieved = work["step"] / d_per_step / (d_launch_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS}
     else:
         achieved = wl.T * work[dom] / d_per_step / (d_launch_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -332,10 +347,15 @@ def main():
     # share of SIMD cycles with the MFMA unit busy (rocprofv3 counters), when fresh
     roof["mfma_busy"] = read_profile_value("mfma_busy", f"{dom}_mfma_busy")
     roof["step_frac"] = tflops / PEAK_BF16_TFLOPS
-    roof["note"] = ("frac is per launch: the plan runs two matrix groups on two streams, so each launch covers "
-                    "half the set and shares the GPU with the other group's launches; step_frac is the whole "
-                    "step's algorithmic rate against the same peak, and roofline_one_stream the kernel's own "
-                    "rate without the overlap")
+    if fused:
+        roof["note"] = ("the fused launch runs every Newton-Schulz product of the step (all T iterations) on one "
+                        "stream; frac is its algorithmic rate over its own duration, step_frac the whole step's "
+                        "(momentum and norm included) against the same peak")
+    else:
+        roof["note"] = ("frac is per launch: the plan runs two matrix groups on two streams, so each launch covers "
+                        "half the set and shares the GPU with the other group's launches; step_frac is the whole "
+                        "step's algorithmic rate against the same peak, and roofline_one_stream the kernel's own "
+                        "rate without the overlap")
 
     out = {
         "metric": "Muon steps/s on GPT-2-small hidden set (T=5); % bf16 MFMA peak",
@@ -352,7 +372,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "gpt2_small_hidden_72", "matrices": n, "params": wl.params, "T": wl.T,
                    "grad_dtype": "bf16", "weight_dtype": "f32", "momentum": wl.momentum, "nesterov": True,
-                   "lr": wl.lr, "coeffs": list(wl.coeffs)},
+                   "lr": wl.lr, "coeffs": list(wl.coeffs), "plan": args.plan},
         "repeats": {"n": args.repeats, "ms_per_step": [round(m, 4) for m in rep_ms_step],
                     "median": rep_ms_step[len(rep_ms_step) // 2], "min": rep_ms_step[0], "max": rep_ms_step[-1],
                     "spread_pct": 100.0 * (rep_ms_step[-1] - rep_ms_step[0]) / rep_ms_step[len(rep_ms_step) // 2],

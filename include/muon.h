@@ -116,6 +116,15 @@ typedef struct muon_options {
                              stream of its own (see muon_plan_info.n_groups).  Two
                              measure fastest on MI355X: with 4 hardware queues per
                              process, more streams start to share queues. */
+  int32_t fused;          /* != 0: a fused plan.  Every bf16 product of a step
+                             (all T iterations of Gram, polynomial and update)
+                             runs in one persistent launch, on the caller's stream
+                             (groups is then ignored): the planner places each
+                             matrix on one XCD, and the launch's blocks take the
+                             tiles of their XCD in order, each waiting until the
+                             tiles it reads are finished (muon_check reports a
+                             wait that gave up).  Steps with T > 16 run the three
+                             launches per iteration instead. */
 } muon_options;
 
 typedef struct muon_plan muon_plan;
@@ -197,7 +206,8 @@ const char* muon_last_error(void);
 #define MUON_KIND_UPDATE 3   /* X <- a X + B X; on the last iteration W <- W - lr s O */
 #define MUON_KIND_APPLY 4    /* T == 0 only: W <- W - lr s X0 */
 #define MUON_KIND_NORM 5     /* T > 0: 1 / (||U||_F + eps) per matrix from the momentum partials */
-#define MUON_KIND_COUNT 6
+#define MUON_KIND_FUSED 6    /* fused plans: every bf16 product of the step in one launch */
+#define MUON_KIND_COUNT 7
 
 /* Host-only description of the plan these descriptors would get.  Returns
  * MUON_OK and fills the fields, or an error code.  `tiles` (optional) gets
@@ -226,6 +236,12 @@ typedef struct muon_plan_info {
                                 multiple of it */
   int32_t bf16_tile_cols;    /* bf16 products: output tile columns (128); the Gram
                                 product takes square tiles of this edge */
+  int32_t fused;             /* 1: a fused plan (muon_options.fused); blocks[MUON_KIND_FUSED]
+                                is then its queue length per iteration (all XCDs),
+                                and kind MUON_KIND_FUSED lists the queue as
+                                (xcd, product 1-3, matrix, tile_row, tile_col)
+                                int32 quintuples, XCD by XCD, each XCD's entries
+                                in the order its blocks take them */
 } muon_plan_info;
 
 int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts,
@@ -244,6 +260,21 @@ int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts
 int muon_profile_enable(muon_plan* plan, int enable);
 int muon_profile_select(muon_plan* plan, uint32_t kind_mask);
 int muon_profile_read(muon_plan* plan, double* ms, int64_t* launches);
+
+/* Fused plans: waits for hip_stream, then reports whether a fused launch of
+ * this plan gave up a dependency wait since the last check (MUON_E_HIP with
+ * the reason; that step's results are incomplete) and clears the report.
+ * MUON_OK otherwise, and always for plans that are not fused.  A wait gives
+ * up after the plan's poll limit (about 4 s by default), which a launch whose
+ * blocks all run never reaches. */
+int muon_check(muon_plan* plan, void* hip_stream);
+
+/* Fused plans, for tests of the give-up path: polls of one dependency wait
+ * before it gives up (> 0; default 1 << 24, 0.25 us apart) and a count added
+ * to every wait's target (>= 0; default 0: with any larger value no wait is
+ * ever met, so every block of the next fused launch gives up and returns).
+ * MUON_E_INVAL for other values or a plan that is not fused. */
+int muon_fused_limits(muon_plan* plan, int32_t spin_limit, int32_t dep_bias);
 
 #ifdef __cplusplus
 }

@@ -20,13 +20,13 @@ MUON_DTYPE_BF16 = 1
 MUON_PATH_BF16 = 0
 MUON_PATH_F32 = 1
 
-KIND_MOMENTUM, KIND_GRAM, KIND_POLY, KIND_UPDATE, KIND_APPLY, KIND_NORM = range(6)
-KIND_COUNT = 6
-KIND_NAMES = ("momentum", "gram", "poly", "update", "apply", "norm")
+KIND_MOMENTUM, KIND_GRAM, KIND_POLY, KIND_UPDATE, KIND_APPLY, KIND_NORM, KIND_FUSED = range(7)
+KIND_COUNT = 7
+KIND_NAMES = ("momentum", "gram", "poly", "update", "apply", "norm", "fused")
 
 EXPORTS = ("muon_version", "muon_workspace_size", "muon_init", "muon_step", "muon_step_schedule", "muon_destroy",
            "muon_last_error", "muon_describe", "muon_profile_enable", "muon_profile_select", "muon_profile_read",
-           "muon_step_scratch")
+           "muon_step_scratch", "muon_check", "muon_fused_limits")
 
 
 class MatrixDesc(ctypes.Structure):
@@ -38,14 +38,15 @@ class MatrixDesc(ctypes.Structure):
 
 class Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("x_master_iters", ctypes.c_int32),
-                ("zero_momentum", ctypes.c_int32), ("max_T", ctypes.c_int32), ("groups", ctypes.c_int32)]
+                ("zero_momentum", ctypes.c_int32), ("max_T", ctypes.c_int32), ("groups", ctypes.c_int32),
+                ("fused", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [("workspace_bytes", ctypes.c_int64), ("n_matrices", ctypes.c_int32), ("tile", ctypes.c_int32),
                 ("blocks", ctypes.c_int32 * KIND_COUNT), ("x_master_iters", ctypes.c_int32),
                 ("path", ctypes.c_int32), ("n_f32_matrices", ctypes.c_int32), ("n_groups", ctypes.c_int32),
-                ("bf16_tile_rows", ctypes.c_int32), ("bf16_tile_cols", ctypes.c_int32)]
+                ("bf16_tile_rows", ctypes.c_int32), ("bf16_tile_cols", ctypes.c_int32), ("fused", ctypes.c_int32)]
 
 
 class MuonError(RuntimeError):
@@ -98,6 +99,10 @@ def load() -> ctypes.CDLL:
     lib.muon_profile_select.argtypes = [ctypes.c_void_p, ctypes.c_uint32]
     lib.muon_profile_read.restype = ctypes.c_int
     lib.muon_profile_read.argtypes = [ctypes.c_void_p, P(ctypes.c_double), P(ctypes.c_int64)]
+    lib.muon_check.restype = ctypes.c_int
+    lib.muon_check.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.muon_fused_limits.restype = ctypes.c_int
+    lib.muon_fused_limits.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
     _lib = lib
     return lib
 

@@ -24,6 +24,7 @@ hipError_t prepare_stage_kernels();
 hipError_t launch_stage_bf16(int stage, const StageArgs& args, int blocks, hipStream_t stream, hipEvent_t ev0,
                              hipEvent_t ev1);
 hipError_t prepare_bf16_kernels();
+hipError_t launch_fused(const FusedArgs& args, int blocks, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_norm(const DevMat* mats, int n, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 }  // namespace muon
 
@@ -68,6 +69,7 @@ struct Options {
   int zero = 0;
   int maxT = 64;
   int groups = 2;
+  int fused = 0;
 };
 
 int read_options(const muon_options* o, Options* out) {
@@ -81,6 +83,8 @@ int read_options(const muon_options* o, Options* out) {
     r.maxT = o->max_T <= 0 ? 64 : o->max_T;
     r.groups = o->groups <= 0 ? 2 : o->groups;
     if (r.groups > kGroups) return fail(MUON_E_INVAL, "options.groups %d exceeds %d", r.groups, kGroups);
+    r.fused = o->fused != 0;
+    if (r.fused) r.groups = 1;  // a fused plan runs on the caller's stream
     if (r.maxT > 4096) return fail(MUON_E_INVAL, "options.max_T %d exceeds 4096", r.maxT);
     if (r.kmaster > 4096) return fail(MUON_E_INVAL, "options.x_master_iters %d exceeds 4096", r.kmaster);
   }
@@ -135,6 +139,9 @@ struct Layout {
   size_t slots = 0, slot_bytes = 0;
   size_t mom_tiles[kGroups] = {};
   size_t ns_tiles[kGroups][2][3] = {};
+  size_t fq = 0;    // fused plans: the XCD queues
+  size_t fctl = 0;  // fused plans: claim counters [kXcds], then the status word
+  size_t fdep = 0;  // fused plans: one finished-tile counter per matrix
   size_t total = 0;
 };
 
@@ -167,6 +174,11 @@ struct Tables {
   std::vector<Tile> mom[kGroups];       // [group]: momentum / apply tiles
   std::vector<Tile> ns[kGroups][2][3];  // [group][precision][kind]
   int first[kGroups + 1] = {};          // group g holds matrices first[g] .. first[g+1]-1
+  // fused plans: one iteration's bf16 tiles per XCD (Tile::pad = product 1-3)
+  std::vector<Tile> fq;                 // XCD by XCD
+  int32_t qoff[kXcds] = {}, qlen[kXcds] = {};
+  std::vector<int> fxcd;                // per matrix: its XCD, -1 when not in the fused launch
+  std::vector<int32_t> fcount[3];       // per matrix: its Gram, polynomial and update tiles per iteration
 };
 
 // Product launches run kXcds * kBlocksPerXcd blocks (two resident blocks on
@@ -264,8 +276,72 @@ void group_bounds(const std::vector<Geometry>& geo, int groups, int (&first)[kGr
   }
 }
 
-Tables build_tables(const std::vector<Geometry>& geo, int groups) {
+// A bf16 matrix's product tiles, each with its cost.  The Gram product takes
+// 128 x 128 tiles on or above the diagonal (a diagonal tile costs a full one:
+// its idle wave keeps pace with the others through the slab barriers).  The
+// polynomial and the update take 256 x 128 tiles (row panel a of 256 rows,
+// column panel b of 128); the polynomial's are those reaching the upper
+// triangle at 128 granularity, b >= 2a, and when b == 2a rows 128..255 lie
+// below it.  Update tiles go column panel by column panel: the tiles of one X
+// column panel run together and share it in L2.
+void bf16_tiles(const Geometry& g, int i, std::vector<CostTile>& gram, std::vector<CostTile>& poly,
+                std::vector<CostTile>& upd) {
+  const double K1 = g.np / 128.0, K2 = g.mp / 128.0;
+  const int tm = g.mp / kTileRowsBf16, tc = g.mp / kTile, tn = g.np / kTile;
+  for (int a = 0; a < tc; ++a)
+    for (int b = a; b < tc; ++b) gram.push_back(CostTile{Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 1}, K1});
+  for (int a = 0; a < tm; ++a)
+    for (int b = 2 * a; b < tc; ++b)
+      poly.push_back(CostTile{Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 2}, (b == 2 * a ? 1.0 : 2.0) * K2});
+  for (int b = 0; b < tn; ++b)
+    for (int a = 0; a < tm; ++a) upd.push_back(CostTile{Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 3}, 2.0 * K2});
+}
+
+// Fused plans: each bf16 matrix goes whole to one XCD, most expensive first,
+// each to the XCD with the least work so far; XCD x's queue lists one
+// iteration's tiles of its matrices, product by product (Gram, polynomial,
+// update), matrix by matrix in placement order within a product.  A
+// product's tiles of the first-placed matrices are therefore the first to
+// have their inputs ready.
+void build_fused(const std::vector<Geometry>& geo, Tables& t) {
+  const int nm = (int)geo.size();
+  t.fxcd.assign(nm, -1);
+  for (int k = 0; k < 3; ++k) t.fcount[k].assign(nm, 0);
+  std::vector<std::vector<CostTile>> tiles[3];
+  for (int k = 0; k < 3; ++k) tiles[k].resize(nm);
+  std::vector<double> cost(nm, 0.0);
+  std::vector<int> order;
+  for (int i = 0; i < nm; ++i) {
+    if (geo[i].f32) continue;
+    bf16_tiles(geo[i], i, tiles[0][i], tiles[1][i], tiles[2][i]);
+    for (int k = 0; k < 3; ++k) {
+      t.fcount[k][i] = (int32_t)tiles[k][i].size();
+      for (const CostTile& c : tiles[k][i]) cost[i] += c.cost;
+    }
+    order.push_back(i);
+  }
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return cost[x] > cost[y]; });
+  double load[kXcds] = {};
+  std::vector<int> on[kXcds];
+  for (int i : order) {
+    const int x = (int)(std::min_element(load, load + kXcds) - load);
+    load[x] += cost[i];
+    on[x].push_back(i);
+    t.fxcd[i] = x;
+  }
+  t.fq.clear();
+  for (int x = 0; x < kXcds; ++x) {
+    t.qoff[x] = (int32_t)t.fq.size();
+    for (int k = 0; k < 3; ++k)
+      for (int i : on[x])
+        for (const CostTile& c : tiles[k][i]) t.fq.push_back(c.t);
+    t.qlen[x] = (int32_t)t.fq.size() - t.qoff[x];
+  }
+}
+
+Tables build_tables(const std::vector<Geometry>& geo, int groups, bool fused) {
   Tables t;
+  if (fused) build_fused(geo, t);
   const int nm = (int)geo.size();
   group_bounds(geo, groups, t.first);
   auto group_of = [&](int i) {
@@ -282,22 +358,7 @@ Tables build_tables(const std::vector<Geometry>& geo, int groups) {
       if (g.f32 != prec || group_of(i) != grp) continue;
       const double K1 = g.np / 128.0, K2 = g.mp / 128.0;
       if (prec == 0) {
-        // bf16: the Gram product takes 128 x 128 tiles on or above the diagonal
-        // (a diagonal tile costs a full one: its idle wave keeps pace with the
-        // others through the slab barriers).  The polynomial and the update
-        // take 256 x 128 tiles (row panel a of 256 rows, column panel b of 128);
-        // the polynomial's are those reaching the upper triangle at 128
-        // granularity, b >= 2a, and when b == 2a rows 128..255 lie below it.
-        const int tm = g.mp / kTileRowsBf16, tc = g.mp / kTile, tn = g.np / kTile;
-        for (int a = 0; a < tc; ++a)
-          for (int b = a; b < tc; ++b) gram[i].push_back(CostTile{Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0}, K1});
-        for (int a = 0; a < tm; ++a)
-          for (int b = 2 * a; b < tc; ++b)
-            poly[i].push_back(CostTile{Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0}, (b == 2 * a ? 1.0 : 2.0) * K2});
-        // update tiles column panel by column panel: the tiles of one X column
-        // panel run together and share it in L2
-        for (int b = 0; b < tn; ++b)
-          for (int a = 0; a < tm; ++a) upd[i].push_back(CostTile{Tile{(uint16_t)i, (uint16_t)a, (uint16_t)b, 0}, 2.0 * K2});
+        bf16_tiles(g, i, gram[i], poly[i], upd[i]);
       } else {
         // fp32: 128 x 128 tiles, upper triangle of the symmetric products
         const int tm = g.mp / kTile, tn = g.np / kTile;
@@ -342,6 +403,14 @@ size_t layout(const std::vector<Geometry>& geo, const Options& o, const Tables& 
         L->ns_tiles[grp][prec][k] = off;
         off = align_up(off + sizeof(Tile) * t.ns[grp][prec][k].size(), kAlign);
       }
+  if (!t.fq.empty()) {
+    L->fq = off;
+    off = align_up(off + sizeof(Tile) * t.fq.size(), kAlign);
+    L->fctl = off;
+    off = align_up(off + sizeof(int32_t) * (kXcds + 1), kAlign);
+    L->fdep = off;
+    off = align_up(off + sizeof(int32_t) * nm, kAlign);
+  }
   L->m.resize(nm);
   for (int i = 0; i < nm; ++i) {
     const Geometry& g = geo[i];
@@ -397,6 +466,8 @@ struct muon_plan {
   bool slot_used[kSlots] = {};
   int slot = 0;
   bool captured = false;  // a step of this plan was enqueued into a capturing stream
+  int32_t spin_limit = 1 << 24;  // fused launch: polls of one dependency wait before it gives up
+  int32_t dep_bias = 0;          // fused launch: added to every wait's target (tests only)
   hipEvent_t last_ev = nullptr;        // recorded after the last enqueued work
   bool last_valid = false;
   hipStream_t gs[kGroups] = {};        // the groups' Newton-Schulz streams (default priority)
@@ -444,6 +515,16 @@ DevMat make_devmat(const muon_plan* p, int i) {
   r.vec_g = (g.cols % 8 == 0) && ((uintptr_t)d.grad % 16 == 0) && ((uintptr_t)d.momentum % 16 == 0);
   r.vec_w = (g.cols % 4 == 0) && ((uintptr_t)d.weight % 16 == 0);
   r.f32 = g.f32;
+  const Tables& t = p->tab;
+  if (!t.fq.empty()) {
+    if (t.fxcd[i] >= 0) {
+      r.dep = (int32_t*)(p->ws + p->lay.fdep) + i;
+      r.ng = t.fcount[0][i];
+      r.npl = t.fcount[1][i];
+      r.nu = t.fcount[2][i];
+    }
+    if (i == 0) r.heads = (int32_t*)(p->ws + p->lay.fctl);  // the norm launch zeroes them with matrix 0's block
+  }
   return r;
 }
 
@@ -519,7 +600,7 @@ size_t muon_workspace_size(const muon_matrix_desc* descs, int n, const muon_opti
   if (validate_all(descs, n, false)) return 0;
   std::vector<Geometry> geo(n);
   for (int i = 0; i < n; ++i) geo[i] = geometry(descs[i], o.path);
-  Tables t = build_tables(geo, o.groups);
+  Tables t = build_tables(geo, o.groups, o.fused);
   Layout L;
   return layout(geo, o, t, &L);
 }
@@ -548,7 +629,7 @@ int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts
   if (rc) return rc;
   std::vector<Geometry> geo(n);
   for (int i = 0; i < n; ++i) geo[i] = geometry(descs[i], o.path);
-  Tables t = build_tables(geo, o.groups);
+  Tables t = build_tables(geo, o.groups, o.fused);
   Layout L;
   const size_t total = layout(geo, o, t, &L);
   if (info) {
@@ -573,8 +654,25 @@ int muon_describe(const muon_matrix_desc* descs, int n, const muon_options* opts
     int ng = 0;
     for (int grp = 0; grp < kGroups; ++grp) ng += !t.mom[grp].empty();
     info->n_groups = ng;
+    info->fused = o.fused;
+    info->blocks[MUON_KIND_FUSED] = (int32_t)t.fq.size();
   }
-  if (kind >= 0) {
+  if (kind == MUON_KIND_FUSED) {
+    if (n_tiles) *n_tiles = (int32_t)t.fq.size();
+    if (tiles) {
+      const int cnt = std::min<int>(tile_cap, (int)t.fq.size());
+      for (int x = 0; x < kXcds; ++x)
+        for (int q = t.qoff[x]; q < t.qoff[x] + t.qlen[x] && q < cnt; ++q) {
+          const Tile& tl = t.fq[q];
+          int32_t* o5 = tiles + 5 * q;
+          o5[0] = x;
+          o5[1] = tl.pad;
+          o5[2] = tl.mat;
+          o5[3] = tl.ti;
+          o5[4] = tl.tj;
+        }
+    }
+  } else if (kind >= 0) {
     std::vector<Tile> v;
     switch (kind) {
       case MUON_KIND_MOMENTUM:
@@ -624,7 +722,7 @@ int muon_init(const muon_matrix_desc* descs, int n, const muon_options* opts, vo
   p->desc.assign(descs, descs + n);
   p->geo.resize(n);
   for (int i = 0; i < n; ++i) p->geo[i] = geometry(descs[i], o.path);
-  p->tab = build_tables(p->geo, o.groups);
+  p->tab = build_tables(p->geo, o.groups, o.fused);
   const size_t need = layout(p->geo, o, p->tab, &p->lay);
   if (ws_bytes < need) {
     delete p;
@@ -665,6 +763,7 @@ int muon_init(const muon_matrix_desc* descs, int n, const muon_options* opts, vo
   for (int grp = 0; grp < kGroups; ++grp)
     for (int prec = 0; prec < 2; ++prec)
       for (int k = 0; k < 3; ++k) lists.push_back({&p->tab.ns[grp][prec][k], p->lay.ns_tiles[grp][prec][k]});
+  lists.push_back({&p->tab.fq, p->lay.fq});
   size_t tb = 0;
   for (auto& l : lists) tb += sizeof(Tile) * l.first->size();
   void* stage = nullptr;
@@ -689,6 +788,13 @@ int muon_init(const muon_matrix_desc* descs, int n, const muon_options* opts, vo
   if (rc) {
     (void)hipHostFree(stage);
     return cleanup(rc);
+  }
+  if (!p->tab.fq.empty()) {  // claim counters and the status word (the norm launch resets the counters)
+    e = hipMemsetAsync(p->ws + p->lay.fctl, 0, sizeof(int32_t) * (kXcds + 1), stream);
+    if (e != hipSuccess) {
+      (void)hipHostFree(stage);
+      return cleanup(hip_fail(e, "hipMemsetAsync(fused counters)"));
+    }
   }
   if (o.zero) {
     for (int i = 0; i < n; ++i) {
@@ -779,6 +885,9 @@ static int enqueue_step(muon_plan* p, const DevMat* mats, const float* sched, fl
   // its own, forked from and joined back into the caller's stream (a single
   // non-empty group stays on the caller's stream).  Starting group 1's
   // momentum pass only after group 0's measured slower.
+  // fused plans run every bf16 product of a step in one launch when the
+  // step's coefficients fit its arguments
+  const bool fuse = !p->tab.fq.empty() && T >= 1 && T <= kFusedMaxT;
   bool busy[kGroups];
   int ngroups = 0;
   for (int grp = 0; grp < kGroups; ++grp) {
@@ -818,7 +927,31 @@ static int enqueue_step(muon_plan* p, const DevMat* mats, const float* sched, fl
       return MUON_OK;
     }
     const int t = (phase - 1) / 3 + 1, k = (phase - 1) % 3;
-    for (int prec = 0; prec < 2; ++prec) {
+    if (fuse && phase == 1) {  // every bf16 product of the step, then the fp32 ones (if any) by launch
+      FusedArgs fa;
+      std::memset(&fa, 0, sizeof(fa));
+      fa.mats = mats;
+      fa.queue = (const Tile*)(p->ws + p->lay.fq);
+      for (int x = 0; x < kXcds; ++x) {
+        fa.qoff[x] = p->tab.qoff[x];
+        fa.qlen[x] = p->tab.qlen[x];
+      }
+      fa.heads = (int32_t*)(p->ws + p->lay.fctl);
+      fa.status = fa.heads + kXcds;
+      fa.T = T;
+      fa.kmaster = p->opt.kmaster;
+      for (int q = 0; q < T; ++q) {
+        fa.coef[q][0] = sched ? sched[3 * q] : a;
+        fa.coef[q][1] = sched ? sched[3 * q + 1] : b;
+        fa.coef[q][2] = sched ? sched[3 * q + 2] : c;
+      }
+      fa.lr = lr;
+      fa.spin_limit = p->spin_limit;
+      fa.dep_bias = p->dep_bias;
+      if ((rc = prof_events(p, MUON_KIND_FUSED, &ev))) return rc;
+      if ((rc = check_launch(launch_fused(fa, kProductGrid, s, ev.start, ev.stop), "fused launch"))) return rc;
+    }
+    for (int prec = fuse ? 1 : 0; prec < 2; ++prec) {
       const int ntab = (int)p->tab.ns[grp][prec][k].size();
       if (!ntab) continue;
       const float* tc = sched ? sched + 3 * (t - 1) : nullptr;
@@ -903,6 +1036,39 @@ int muon_profile_select(muon_plan* p, uint32_t kind_mask) {
   return MUON_OK;
 }
 
+int muon_check(muon_plan* p, void* hip_stream) {
+  g_err.clear();
+  if (!p) return fail(MUON_E_INVAL, "plan is NULL");
+  if (p->tab.fq.empty()) return MUON_OK;
+  hipStream_t stream = (hipStream_t)hip_stream;
+  int32_t* status = (int32_t*)(p->ws + p->lay.fctl) + kXcds;
+  int32_t h = 0;
+  hipError_t e = hipMemcpyAsync(&h, status, sizeof(h), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "muon_check: reading the fused launch status");
+  if (h == 0) return MUON_OK;
+  e = hipMemsetAsync(status, 0, sizeof(int32_t), stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "muon_check: clearing the fused launch status");
+  if (h & kFusedBadEntry)
+    return fail(MUON_E_HIP, "fused launch: a queue entry lies outside its matrix (status %d); the blocks stopped "
+                "and that step's results are incomplete", (int)h);
+  return fail(MUON_E_HIP,
+              "fused launch: a dependency wait gave up after %d polls (status %d); the blocks stopped and that "
+              "step's results are incomplete",
+              p->spin_limit, (int)h);
+}
+
+int muon_fused_limits(muon_plan* p, int32_t spin_limit, int32_t dep_bias) {
+  g_err.clear();
+  if (!p) return fail(MUON_E_INVAL, "plan is NULL");
+  if (p->tab.fq.empty()) return fail(MUON_E_INVAL, "the plan is not fused");
+  if (spin_limit <= 0 || dep_bias < 0) return fail(MUON_E_INVAL, "spin_limit %d must be > 0, dep_bias %d >= 0", spin_limit, dep_bias);
+  p->spin_limit = spin_limit;
+  p->dep_bias = dep_bias;
+  return MUON_OK;
+}
+
 int muon_profile_read(muon_plan* p, double* ms, int64_t* launches) {
   g_err.clear();
   if (!p) return fail(MUON_E_INVAL, "plan is NULL");
@@ -984,6 +1150,7 @@ int muon_step_scratch(const muon_matrix_desc* descs, int n, const muon_options* 
   if (rc) return rc;
   if (o.zero) return fail(MUON_E_INVAL, "options.zero_momentum is not supported by muon_step_scratch");
   o.groups = 1;  // one stream: the caller's
+  o.fused = 0;   // the three launches per iteration: a fused launch keeps per-plan counters
   if (T < 0 || T > o.maxT) return fail(MUON_E_INVAL, "T=%d outside [0, max_T=%d]", T, o.maxT);
   if (!std::isfinite(a) || !std::isfinite(b) || !std::isfinite(c)) return fail(MUON_E_INVAL, "a, b and c must be finite");
   if (!std::isfinite(lr)) return fail(MUON_E_INVAL, "lr must be finite");
@@ -997,7 +1164,7 @@ int muon_step_scratch(const muon_matrix_desc* descs, int n, const muon_options* 
   p.desc.assign(descs, descs + n);
   p.geo.resize(n);
   for (int i = 0; i < n; ++i) p.geo[i] = geometry(descs[i], o.path);
-  p.tab = build_tables(p.geo, o.groups);
+  p.tab = build_tables(p.geo, o.groups, false);
   const size_t need = layout(p.geo, o, p.tab, &p.lay);
   if (need > kScratchBytes)
     return fail(MUON_E_WORKSPACE, "this step needs %zu bytes of scratch; muon_step_scratch holds %zu (use muon_init "

@@ -552,7 +552,9 @@ __global__ __launch_bounds__(kThreads) void norm_kernel(const DevMat* mats) {
   if (threadIdx.x == 0) {
     gv<float>(d.sc)[0] = inv;
     gv<float>(d.sc)[1] = (float)nu;
+    if (d.dep) *gv<int32_t>(d.dep) = 0;  // the fused launch's counters start each step at zero
   }
+  if (d.heads && threadIdx.x < kXcds) gv<int32_t>(d.heads)[threadIdx.x] = 0;
 }
 
 // Where a tile's operand panels are, and its K extent (wave-uniform).  A

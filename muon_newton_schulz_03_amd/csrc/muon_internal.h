@@ -51,6 +51,11 @@ struct DevMat {
   int32_t vec_w;      // weight rows can be read/written 4 elements at a time
   int32_t f32;        // this matrix's products use fp32 operands (xo, a, b are fp32)
   int32_t pad_;
+  // fused launch (bf16 matrices of a fused plan; null / 0 otherwise)
+  int32_t* dep;       // tiles of this matrix finished in the current step
+  int32_t* heads;     // set on the first matrix only: the fused launch's claim counters, zeroed with dep
+  int32_t ng, npl, nu;// the matrix's Gram, polynomial and update tiles per iteration
+  int32_t pad2_;
 };
 
 struct Tile {
@@ -69,6 +74,28 @@ struct StageArgs {
   int32_t kmaster;  // bf16 path: iterations 1..kmaster read X as its (bf16, low byte) pair in a*X
   float a, b, c;
   float lr;
+};
+
+// The fused launch: every bf16 product of a step in one persistent launch.
+// XCD x works through its queue, one iteration's tiles (Gram, then
+// polynomial, then update, of the matrices placed on it) repeated T times;
+// blocks claim the next entry from heads[x] and wait until the tiles it reads
+// are finished (per-matrix counters in DevMat::dep).
+constexpr int kFusedMaxT = 16;  // iterations whose coefficients fit the launch arguments
+enum { kFusedWaitGaveUp = 1, kFusedBadEntry = 2 };  // FusedArgs::status bits
+struct FusedArgs {
+  const DevMat* mats;
+  const Tile* queue;            // Tile::pad = product (1 Gram, 2 polynomial, 3 update)
+  int32_t qoff[kXcds];          // XCD x: one iteration's entries at queue[qoff[x] .. qoff[x] + qlen[x])
+  int32_t qlen[kXcds];
+  int32_t* heads;               // [kXcds] entries claimed so far this step
+  int32_t* status;              // 0, or why a block gave up (sticky until read)
+  int32_t T, kmaster;
+  float coef[kFusedMaxT][3];    // (a, b, c) of iteration t at coef[t - 1]
+  float lr;
+  int32_t spin_limit;           // polls of one dependency wait before it gives up
+  int32_t dep_bias;             // added to every wait's target (0; a test of the give-up path raises it)
+  int32_t pad_;
 };
 
 struct MomArgs {

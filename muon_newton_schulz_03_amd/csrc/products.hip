@@ -664,6 +664,126 @@ struct Epi {
   }
 };
 
+// Requests of a tile's first slabs (and of its first low bytes) into ring
+// slots 0 .. kAhead - 1 and low-byte buffer 0: the start of a block's run of
+// tiles, with nothing of the ring in flight.
+template <int STAGE, int MODE>
+__device__ __forceinline__ void tile_prologue(char* smem, const Ctx& c, int w, int lane) {
+  if (STAGE == 3 && (MODE & kHiLo)) issue_lo(smem, c, 0, 0, w, lane);
+#pragma unroll
+  for (int d = 0; d < Shape<STAGE>::kAhead; ++d) issue_slab<STAGE>(smem, c, d, d, w, lane);
+}
+
+// One tile: its K loop, whose last slabs request the first slabs of the
+// block's next tile `cn` (cn.p == nullptr: empty requests, which keep the
+// wait counts static), and its epilogue.  `g` counts the slabs the block has
+// consumed (ring slot g % kRing, low-byte buffer g % 2); `pend` is the number
+// of the previous epilogue's instructions issued after this tile's first
+// kAhead slabs.  Returns the instructions this tile's epilogue issued after
+// the next tile's first slabs.
+template <int STAGE, int MODE>
+__device__ __forceinline__ int tile_pass(const StageArgs& args, char* smem, const Tile& tl, const Ctx& c,
+                                         const Ctx& cn, int& g, int pend, int w, int wm, int wn, int lane,
+                                         const FragOff& fo) {
+  using E = Epi<STAGE, MODE>;
+  using G = Shape<STAGE>;
+  constexpr bool kLoIn = STAGE == 3 && (MODE & kHiLo);
+  constexpr int kDepth = E::kDepth;
+  constexpr int kAhead = G::kAhead;
+  constexpr int kD = G::kDma;  // requests per wave per slab
+  // on a diagonal tile of stages 1 and 2, waves whose rows lie wholly below
+  // the diagonal only move data
+  const bool idle = STAGE != 3 && (G::kWide ? wm == 1 && c.skip1 : c.psrc && wm == 1 && wn == 0);
+  const int R0 = c.i0 + (G::kRows / 2) * wm;
+  float alpha = args.a;
+  if (STAGE == 3 && args.t == 1) alpha *= load_uniform(load_uniform(&args.mats[tl.mat].sc));
+  typename E::In in[E::kInSlots];
+
+  f32x16 acc[G::kMI][2];
+#pragma unroll
+  for (int mi = 0; mi < G::kMI; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < 2; ++nj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][nj][v] = 0.f;
+
+  // K slabs: at least kAhead (Gram: K = np >= 128, four slabs); stage 2 has
+  // K = mp >= 256, so its first and last kAhead slabs never overlap
+  const int nk = c.nk;
+  // stage 2: the epilogue's first A requests, made as slab nk - kAhead starts
+  const int early = STAGE == 2 && !idle ? kDepth * 2 : 0;
+  int vm_pre = 0;  // instructions issued after those requests
+  for (int kt = 0; kt < nk; ++kt) {
+    // this wave's part of slab kt (and its low bytes) has landed: only the
+    // slabs requested after it may still be in flight, plus, at the first
+    // slabs of a tile, the previous epilogue's instructions, and at the last
+    // slabs of stage 2, the early A requests
+    if (STAGE == 3) {
+      if (kt == 0 || (kt == 1 && !kLoIn))
+        wait_vm(kD + pend);
+      else
+        MUON_WAIT_VMCNT(kD);
+    } else if (kt < kAhead) {
+      wait_vm((kAhead - 1) * kD + pend);
+    } else if (STAGE == 2 && kt > nk - kAhead) {
+      wait_vm((kAhead - 1) * kD + early);
+    } else {
+      MUON_WAIT_VMCNT((kAhead - 1) * kD);
+    }
+    MUON_LDS_BARRIER();  // every wave's part has landed; slab kt - 1's slot is free
+    if (kLoIn) issue_lo(smem, kt + 1 < nk ? c : cn, kt + 1 < nk ? kt + 1 : kt + 1 - nk, (g + 1) & 1, w, lane);
+    if (STAGE == 2 && kt == nk - kAhead && !idle) {  // the epilogue's first inputs
+      const E ep(args, args.mats + tl.mat, c, wm, wn, lane);
+#pragma unroll
+      for (int b = 0; b < kDepth; ++b) ep.load(b, in[b % E::kInSlots]);
+    }
+    const int slot = (g + kAhead) % G::kRing;
+    if (kt + kAhead < nk)
+      issue_slab<STAGE>(smem, c, kt + kAhead, slot, w, lane);
+    else
+      issue_slab<STAGE>(smem, cn, kt + kAhead - nk, slot, w, lane);
+    if (STAGE == 2 && kt >= nk - kAhead) vm_pre += kD;
+    const char* s = smem + (g % G::kRing) * G::kSlot;
+    if (!idle) {
+      const char* p = c.psrc ? s + (c.psrc - 1) * kHalf : s + G::kPOff;
+      if (STAGE == 3) {
+        const int rel = kt * kBK - R0;  // this slab's K rows are output rows of the wave
+        if (rel >= 0 && rel < 128) {
+          const char* lo = smem + kLoBase + (g & 1) * kLoBuf;
+          switch (rel >> 5) {
+            case 0: fold_x<kLoIn>(acc[0], p, lo, wn, lane, alpha); break;
+            case 1: fold_x<kLoIn>(acc[1], p, lo, wn, lane, alpha); break;
+            case 2: fold_x<kLoIn>(acc[2 % G::kMI], p, lo, wn, lane, alpha); break;
+            default: fold_x<kLoIn>(acc[3 % G::kMI], p, lo, wn, lane, alpha); break;
+          }
+        }
+        mma_slab<true, G::kMI>(acc, s + wm * kHalf, p, wn, lane, fo);
+      } else {
+        mma_slab<false, G::kMI>(acc, s + wm * (G::kWide ? kHalf : kHalf / 2), p, wn, lane, fo);
+      }
+    }
+    ++g;
+  }
+
+  // epilogue: the last slab's slot holds the waves' staged blocks
+  MUON_LDS_BARRIER();  // all waves are done with the last slab
+  int issued = 0;
+  if (!idle) {
+    const E ep(args, args.mats + tl.mat, c, wm, wn, lane);
+    int early_w = 0;  // requests made after the next tile's first slabs, before run()
+    if (E::kLastIt) {  // the weight step requests its first W blocks here (registers are short in the loop)
+#pragma unroll
+      for (int b = 0; b < kDepth; ++b) ep.load(b, in[b % E::kInSlots]);
+      vm_pre = 0;
+      early_w = kDepth * ep.loads_per_block();
+    }
+    Stage st;
+    st.base = smem + ((g + G::kRing - 1) % G::kRing) * G::kSlot + w * kBlock;
+    issued = early_w + ep.run(acc, st, in, vm_pre);
+  }
+  return issued;
+}
+
 // Persistent product kernel: block b takes the table entries b, b + G,
 // b + 2 G, ... (G = gridDim.x, a multiple of 8: every entry stays on the XCD
 // the table placed it on).
@@ -801,6 +921,153 @@ __global__ __launch_bounds__(kThreads, kBlocks) void ns_bf16_kernel(StageArgs ar
   }
 }
 
+// ---------------------------------------------------------- fused launch --
+//
+// One persistent launch runs every bf16 product of a step.  The planner puts
+// each matrix, with all of its tiles, on one XCD; XCD x's queue is one
+// iteration's tiles of its matrices (Gram, then polynomial, then update),
+// repeated T times.  A block reads the XCD it runs on from the hardware, takes
+// the next entry of that XCD's queue (an atomic counter), waits until the
+// tiles the entry reads are finished, runs the tile and counts it finished in
+// its matrix's counter.  Tile (t, product) of a matrix reads what the
+// previous product of iteration t (or the update of iteration t - 1) wrote,
+// so it waits for the counter to reach the tiles of everything before it:
+//   Gram t:    (t - 1) (ng + npl + nu)
+//   poly t:    (t - 1) (ng + npl + nu) + ng
+//   update t:  (t - 1) (ng + npl + nu) + ng + npl
+// and that also orders every overwrite after the reads of the old contents
+// (A, B and X's two copies are reused every iteration).
+//
+// Progress: entries are claimed in queue order and every wait is for entries
+// earlier in the same queue, so the earliest unfinished entry is always
+// either claimed by a running block whose waits are met or next to be
+// claimed; no block ever waits for a block that is not running.  Each wait is
+// still bounded: after spin_limit polls the block sets the status word and
+// stops, and so does every block that sees the status set.
+//
+// Memory: producer and consumer of a matrix's data run on one XCD and share
+// its L2.  A finished tile's stores are complete (vmcnt 0) before its counter
+// moves; a block that waited invalidates at agent scope (buffer_inv sc1)
+// before requesting the tile's operands: the group-scope form (sc0) left
+// stale operand data visible on MI355X (results differed from the three-launch
+// plan's), the agent-scope form makes them bitwise equal.
+
+// Thread 0: wait until `dep` reaches `need` (true), or give up (false).
+__device__ __noinline__ bool fused_wait(int32_t* dep, int need, int32_t* status, int limit) {
+  for (int spins = 0;; ++spins) {
+    if (__hip_atomic_load(dep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) return true;
+    if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return false;
+    if (spins >= limit) {
+      __hip_atomic_fetch_or(status, (int)kFusedWaitGaveUp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
+// One tile of the fused launch, on its own: the ring starts empty and the
+// tile's epilogue stores are complete when it returns.
+template <int STAGE, int MODE>
+__device__ __forceinline__ void fused_tile(const StageArgs& args, char* smem, const Tile& tl, int w, int wm, int wn,
+                                           int lane, const FragOff& fo) {
+  const Ctx c = ctx_of<STAGE, MODE>(args, tl);
+  Ctx cn = c;
+  cn.p = nullptr;  // no next tile: empty requests
+  tile_prologue<STAGE, MODE>(smem, c, w, lane);
+  int g = 0;
+  (void)tile_pass<STAGE, MODE>(args, smem, tl, c, cn, g, 0, w, wm, wn, lane, fo);
+  MUON_WAIT_VMCNT(0);
+}
+
+__global__ __launch_bounds__(kThreads, kBlocks) void ns_fused_kernel(FusedArgs fa) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  volatile int32_t* ctl = (volatile int32_t*)smem;  // between tiles the LDS is free: claim and verdict
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int w = __builtin_amdgcn_readfirstlane(wave);
+  const int lane = threadIdx.x & 63;
+  const FragOff fo = frag_off(lane);
+  int hw;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(hw));
+  const int x = hw & (kXcds - 1);
+  const int per = fa.qlen[x];
+  const int total = per * fa.T;
+  const Tile* queue = fa.queue + fa.qoff[x];
+  for (;;) {
+    if (threadIdx.x == 0) {
+      const bool stop = __hip_atomic_load(fa.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+      ctl[0] = stop ? total : __hip_atomic_fetch_add(fa.heads + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    MUON_LDS_BARRIER();
+    const int e = __builtin_amdgcn_readfirstlane(ctl[0]);
+    if (e >= total) break;
+    const int t = e / per + 1;
+    const uint64_t raw = *(const MUON_CONST uint64_t*)(const void*)(queue + (e - (t - 1) * per));
+    const Tile tl = tile_of(raw);
+    const int stage = (int)(raw >> 48);  // Tile::pad: the product (tile_of leaves it out)
+    const DevMat* m = fa.mats + tl.mat;
+    int32_t* dep = load_uniform(&m->dep);
+    {
+      // the tile must lie inside its matrix (the epilogues' stores are not
+      // bounds-checked): an entry that does not is reported, never run
+      const int mp = load_uniform(&m->mp), np = load_uniform(&m->np);
+      const int ti = tl.ti, tj = tl.tj;
+      bool valid = dep != nullptr;
+      if (stage == 1) valid = valid && ti <= tj && tj < mp / 128;
+      else if (stage == 2) valid = valid && 2 * ti <= tj && tj < mp / 128;
+      else if (stage == 3) valid = valid && ti < mp / 256 && tj < np / 128;
+      else valid = false;
+      if (!valid) {
+        if (threadIdx.x == 0)
+          __hip_atomic_fetch_or(fa.status, (int)kFusedBadEntry, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+    if (threadIdx.x == 0) {
+      const int ng = load_uniform(&m->ng), npl = load_uniform(&m->npl), nu = load_uniform(&m->nu);
+      const int need = (t - 1) * (ng + npl + nu) + (stage >= 2 ? ng : 0) + (stage == 3 ? npl : 0) + fa.dep_bias;
+      ctl[1] = fused_wait(dep, need, fa.status, fa.spin_limit) ? 1 : 0;
+    }
+    MUON_LDS_BARRIER();
+    const int ok = __builtin_amdgcn_readfirstlane(ctl[1]);
+    asm volatile("buffer_inv sc1" ::: "memory");
+    MUON_LDS_BARRIER();  // every wave has read ctl before the tile's requests land over it
+    if (!ok) break;
+    StageArgs sa;
+    sa.mats = fa.mats;
+    sa.tiles = nullptr;
+    sa.ntiles = 0;
+    sa.t = t;
+    sa.T = fa.T;
+    sa.kmaster = fa.kmaster;
+    sa.a = fa.coef[t - 1][0];
+    sa.b = fa.coef[t - 1][1];
+    sa.c = fa.coef[t - 1][2];
+    sa.lr = fa.lr;
+    if (stage == 1) {
+      fused_tile<1, 0>(sa, smem, tl, w, wm, wn, lane, fo);
+    } else if (stage == 2) {
+      fused_tile<2, 0>(sa, smem, tl, w, wm, wn, lane, fo);
+    } else {  // stage 3 (checked above)
+      const bool last = t == fa.T, hilo = t <= fa.kmaster, write_lo = !last && t < fa.kmaster;
+      if (last) {
+        if (hilo)
+          fused_tile<3, kHiLo | kLast>(sa, smem, tl, w, wm, wn, lane, fo);
+        else
+          fused_tile<3, kLast>(sa, smem, tl, w, wm, wn, lane, fo);
+      } else if (write_lo) {
+        fused_tile<3, kHiLo | kWriteLo>(sa, smem, tl, w, wm, wn, lane, fo);
+      } else if (hilo) {
+        fused_tile<3, kHiLo>(sa, smem, tl, w, wm, wn, lane, fo);
+      } else {
+        fused_tile<3, 0>(sa, smem, tl, w, wm, wn, lane, fo);
+      }
+    }
+    MUON_BARRIER();  // every wave's stores are complete
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(dep, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------ launchers --
@@ -809,7 +1076,7 @@ __global__ __launch_bounds__(kThreads, kBlocks) void ns_bf16_kernel(StageArgs ar
 hipError_t prepare_bf16_kernels() {
   const void* fns[] = {MUON_BF16_KERNEL(1, 0), MUON_BF16_KERNEL(2, 0), MUON_BF16_KERNEL(3, 0),
                        MUON_BF16_KERNEL(3, 1), MUON_BF16_KERNEL(3, 5), MUON_BF16_KERNEL(3, 2),
-                       MUON_BF16_KERNEL(3, 3)};
+                       MUON_BF16_KERNEL(3, 3), (const void*)ns_fused_kernel};
   for (const void* f : fns) {
     hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     if (e != hipSuccess) return e;
@@ -821,6 +1088,12 @@ static hipError_t launch_bf16(const void* fn, int blocks, const StageArgs& args,
                               hipEvent_t ev1) {
   void* kargs[] = {(void*)&args};
   return hipExtLaunchKernel(fn, dim3(blocks), dim3(kThreads), kargs, kLds, stream, ev0, ev1, 0);
+}
+
+hipError_t launch_fused(const FusedArgs& args, int blocks, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  void* kargs[] = {(void*)&args};
+  return hipExtLaunchKernel((const void*)ns_fused_kernel, dim3(blocks), dim3(kThreads), kargs, kLds, stream, ev0, ev1,
+                            0);
 }
 
 hipError_t launch_stage_bf16(int stage, const StageArgs& args, int blocks, hipStream_t stream, hipEvent_t ev0,

@@ -25,10 +25,11 @@ def version() -> str:
     return _lib.load().muon_version().decode()
 
 
-def _options(path: str, x_master_iters: int, zero_momentum: bool, max_T: int, groups: int = 0) -> Options:
+def _options(path: str, x_master_iters: int, zero_momentum: bool, max_T: int, groups: int = 0,
+             fused: bool = False) -> Options:
     if path not in _PATHS:
         raise ValueError(f"path must be one of {sorted(_PATHS)}")
-    return Options(_PATHS[path], x_master_iters, int(zero_momentum), max_T, groups)
+    return Options(_PATHS[path], x_master_iters, int(zero_momentum), max_T, groups, int(bool(fused)))
 
 
 def _desc_array(shapes_dtypes, ptrs=None, scales=None) -> ctypes.Array:
@@ -69,11 +70,13 @@ def _tensor_descs(weights, grads, moms, scales) -> ctypes.Array:
 
 def describe(shapes: Sequence[Tuple[int, int]], path: str = "bf16", x_master_iters: int = -1,
              kind: Optional[int] = None, grad_dtype=torch.bfloat16, weight_dtype=torch.float32,
-             groups: int = 0) -> Tuple[dict, list]:
-    """Host-only plan description (no GPU needed): sizes, grids and one tile list."""
+             groups: int = 0, fused: bool = False) -> Tuple[dict, list]:
+    """Host-only plan description (no GPU needed): sizes, grids and one tile list
+    ((matrix, tile_row, tile_col) triples; for KIND_FUSED (xcd, product, matrix,
+    tile_row, tile_col) quintuples)."""
     lib = _lib.load()
     arr = _desc_array([(r, c, _DTYPES[weight_dtype], _DTYPES[grad_dtype]) for r, c in shapes])
-    opts = _options(path, x_master_iters, False, 0, groups)
+    opts = _options(path, x_master_iters, False, 0, groups, fused)
     info = PlanInfo()
     count = ctypes.c_int32(0)
     k = -1 if kind is None else kind
@@ -81,14 +84,15 @@ def describe(shapes: Sequence[Tuple[int, int]], path: str = "bf16", x_master_ite
                                  ctypes.byref(count)))
     tiles = []
     if kind is not None and count.value:
-        buf = (ctypes.c_int32 * (3 * count.value))()
+        width = 5 if k == _lib.KIND_FUSED else 3
+        buf = (ctypes.c_int32 * (width * count.value))()
         _lib.check(lib.muon_describe(arr, len(shapes), ctypes.byref(opts), None, k, buf, count.value,
                                      ctypes.byref(count)))
-        tiles = [tuple(buf[3 * q:3 * q + 3]) for q in range(count.value)]
+        tiles = [tuple(buf[width * q:width * q + width]) for q in range(count.value)]
     d = dict(workspace_bytes=info.workspace_bytes, n_matrices=info.n_matrices, tile=info.tile,
              blocks=list(info.blocks), x_master_iters=info.x_master_iters, path=info.path,
              n_f32_matrices=info.n_f32_matrices, n_groups=info.n_groups,
-             bf16_tile_rows=info.bf16_tile_rows, bf16_tile_cols=info.bf16_tile_cols)
+             bf16_tile_rows=info.bf16_tile_rows, bf16_tile_cols=info.bf16_tile_cols, fused=info.fused)
     return d, tiles
 
 
@@ -119,7 +123,7 @@ class MuonStep:
     def __init__(self, weights: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
                  moms: Sequence[torch.Tensor], *, path: str = "bf16", x_master_iters: int = -1,
                  zero_momentum: bool = False, max_T: int = 0, scales: Optional[Sequence[float]] = None,
-                 groups: int = 0):
+                 groups: int = 0, fused: bool = False):
         self._lib = _lib.load()
         self.n = len(weights)
         if self.n == 0:
@@ -128,7 +132,7 @@ class MuonStep:
         self.scales = None if scales is None else list(scales)
         self._descs = _tensor_descs(weights, grads, moms, self.scales)
         self._keep = (list(weights), list(grads), list(moms))
-        self._opts = _options(path, x_master_iters, zero_momentum, max_T, groups)
+        self._opts = _options(path, x_master_iters, zero_momentum, max_T, groups, fused)
         ws = self._lib.muon_workspace_size(self._descs, self.n, ctypes.byref(self._opts))
         if ws == 0:
             raise _lib.MuonError(_lib.MUON_E_INVAL, _lib.last_error())
@@ -170,6 +174,15 @@ class MuonStep:
             return
         _lib.check(self._lib.muon_step(self._plan, descs, self.n, a, b, c, int(T), momentum, int(bool(nesterov)),
                                        lr, ctypes.c_void_p(stream)))
+
+    def check(self) -> None:
+        """Wait for the current stream; raise if a fused launch gave up a dependency wait."""
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        _lib.check(self._lib.muon_check(self._plan, ctypes.c_void_p(stream)))
+
+    def fused_limits(self, spin_limit: int, dep_bias: int = 0) -> None:
+        """Poll limit and target bias of the fused launch's dependency waits (tests of the give-up path)."""
+        _lib.check(self._lib.muon_fused_limits(self._plan, int(spin_limit), int(dep_bias)))
 
     def profile(self, enable: bool = True, kinds: Optional[Sequence[str]] = None) -> None:
         """Time launches with HIP events; ``kinds`` (names from KIND_NAMES) limits which."""

@@ -50,6 +50,7 @@ KINDS = {
     "ns_stage_kernel<2": "poly",
     "ns_stage_kernel<3": "update",
     "apply_kernel": "apply",
+    "ns_fused_kernel": "fused",
 }
 
 

@@ -305,3 +305,70 @@ def test_init_reports_hip_failures(lib):
                  ctypes.byref(plan), match=r"^hip\w+\(.*\): .+ \(\d+\)$")
     assert not plan.value
     assert "device" in _lib.last_error()
+
+
+FUSED_SETS = [
+    inputs.workload("gpt2_small").shapes,
+    [(300, 700), (700, 300), (129, 4100), (1000, 130), (64, 64), (100, 333), (256, 256), (512, 1536)],
+    [(768, 768)],
+    [(4, 8), (100, 100)],  # only fp32 products: an empty queue
+]
+
+
+@pytest.mark.parametrize("shapes", FUSED_SETS, ids=["gpt2_small", "mixed", "one", "fp32_only"])
+def test_fused_queues(shapes):
+    """The fused plan's per-XCD queues: every bf16 matrix's tiles of each
+    product exactly once, all on one XCD, each XCD's entries product by
+    product (Gram 1, polynomial 2, update 3), every tile inside its matrix (the
+    ranges the kernel checks before it runs an entry), no fp32 matrix."""
+    d, q = describe(shapes, kind=_lib.KIND_FUSED, fused=True)
+    assert d["fused"] == 1 and d["n_groups"] == 1
+    assert d["blocks"][_lib.KIND_FUSED] == len(q)
+    xcd_of = {}
+    per = {}
+    last_product = {}
+    for x, prod, i, ti, tj in q:
+        assert 0 <= x < 8 and prod in (1, 2, 3)
+        assert xcd_of.setdefault(i, x) == x, f"matrix {i} on two XCDs"
+        assert prod >= last_product.get(x, 1), f"XCD {x}: product {prod} after {last_product[x]}"
+        last_product[x] = prod
+        per.setdefault((i, prod), []).append((ti, tj))
+    kinds = {1: _lib.KIND_GRAM, 2: _lib.KIND_POLY, 3: _lib.KIND_UPDATE}
+    for i, (r, c) in enumerate(shapes):
+        m, n = min(r, c), max(r, c)
+        if m < 128:
+            assert i not in xcd_of
+            continue
+        mp, np_ = -(-m // 256) * 256, -(-n // 128) * 128
+        for prod, kind in kinds.items():
+            got = per[(i, prod)]
+            assert len(got) == len(set(got))
+            assert {(0, a, b) for a, b in got} == expected_tiles([(r, c)], kind)  # the staged plan's tiles
+            for ti, tj in got:
+                if prod == 1:
+                    assert ti <= tj < mp // 128
+                elif prod == 2:
+                    assert 2 * ti <= tj < mp // 128
+                else:
+                    assert ti < mp // 256 and tj < np_ // 128
+
+
+def test_fused_queues_balance_gpt2_small():
+    """The 72 GPT-2 small matrices spread over the 8 XCDs with equal work
+    (3 of 768 x 3072 and 6 of 768 x 768 on each)."""
+    shapes = inputs.workload("gpt2_small").shapes
+    _, q = describe(shapes, kind=_lib.KIND_FUSED, fused=True)
+    mats = {}
+    for x, prod, i, ti, tj in q:
+        mats.setdefault(x, set()).add(i)
+    assert len(mats) == 8
+    for x, s in mats.items():
+        big = sum(1 for i in s if max(shapes[i]) == 3072)
+        assert (big, len(s) - big) == (3, 6), f"XCD {x}: {big} large, {len(s) - big} small"
+
+
+def test_fused_entry_points_reject_bad_arguments(lib):
+    assert lib.muon_check(None, None) == _lib.MUON_E_INVAL
+    assert lib.muon_fused_limits(None, 1, 0) == _lib.MUON_E_INVAL
+    d, _ = describe([(768, 768)], fused=False)
+    assert d["fused"] == 0 and d["blocks"][_lib.KIND_FUSED] == 0
