@@ -145,9 +145,9 @@ int muon_init(const muon_matrix_desc* descs, int n, const muon_options* opts,
               void* workspace, size_t ws_bytes, void* hip_stream, muon_plan** out_plan);
 
 /* Enqueue one Muon step over every matrix of the plan on hip_stream.  Per
- * matrix group (muon_plan_info.n_groups; each group on a stream of its own,
- * forked from and joined back into hip_stream, so later work on hip_stream
- * sees the whole step): 1 momentum launch and 1 norm launch, then 3 launches
+ * matrix group (muon_plan_info.n_groups; the first group on hip_stream itself,
+ * each other one on a stream of its own, forked from and joined back into
+ * hip_stream, so later work on hip_stream sees the whole step): 1 momentum launch and 1 norm launch, then 3 launches
  * per Newton-Schulz iteration (all matrices of one precision grouped in each
  * launch: 6 per iteration when the group mixes bf16 and fp32 matrices); T == 0
  * enqueues one weight-step launch instead of norm and iterations

@@ -882,9 +882,9 @@ static int enqueue_step(muon_plan* p, const DevMat* mats, const float* sched, fl
   int rc;
 
   // Each group's whole step (momentum, norm, T iterations) runs on a stream of
-  // its own, forked from and joined back into the caller's stream (a single
-  // non-empty group stays on the caller's stream).  Starting group 1's
-  // momentum pass only after group 0's measured slower.
+  // its own: the first on the caller's stream, the others forked from it and
+  // joined back into it.  Starting group 1's momentum pass only after group
+  // 0's measured slower.
   // fused plans run every bf16 product of a step in one launch when the
   // step's coefficients fit its arguments
   const bool fuse = !p->tab.fq.empty() && T >= 1 && T <= kFusedMaxT;
@@ -894,12 +894,18 @@ static int enqueue_step(muon_plan* p, const DevMat* mats, const float* sched, fl
     busy[grp] = !p->tab.mom[grp].empty();
     ngroups += busy[grp];
   }
+  // The first busy group runs on the caller's stream itself: between two
+  // steps it then waits for one event hop (the other groups' joins) instead of
+  // three (joins, fork record, fork wait); measured 1.87 against 1.90 ms.
   const bool fork = ngroups > 1;
+  int home = 0;
+  while (home < kGroups && !busy[home]) ++home;
+  auto group_stream = [&](int grp) { return !fork || grp == home ? stream : p->gs[grp]; };
   hipError_t e = hipSuccess;
   if (fork) {
     e = hipEventRecord(p->fork_ev, stream);
     for (int grp = 0; grp < kGroups && e == hipSuccess; ++grp)
-      if (busy[grp]) e = hipStreamWaitEvent(p->gs[grp], p->fork_ev, 0);
+      if (busy[grp] && grp != home) e = hipStreamWaitEvent(p->gs[grp], p->fork_ev, 0);
     if (e != hipSuccess) return hip_fail(e, "fork of the group streams");
   }
   // Launch phase 0 is momentum plus norm (or apply when T = 0); phase
@@ -908,7 +914,7 @@ static int enqueue_step(muon_plan* p, const DevMat* mats, const float* sched, fl
   // group stream has work queued early even when the host enqueues slower
   // than the GPU runs.
   auto enqueue = [&](int grp, int phase) -> int {
-    hipStream_t s = fork ? p->gs[grp] : stream;
+    hipStream_t s = group_stream(grp);
     if (phase == 0) {
       const Tile* mom_tiles = (const Tile*)(p->ws + p->lay.mom_tiles[grp]);
       const int nmom = (int)p->tab.mom[grp].size();
@@ -972,7 +978,7 @@ static int enqueue_step(muon_plan* p, const DevMat* mats, const float* sched, fl
       if (busy[grp] && (rc = enqueue(grp, phase))) return rc;
   if (fork) {
     for (int grp = 0; grp < kGroups; ++grp) {
-      if (!busy[grp]) continue;
+      if (!busy[grp] || grp == home) continue;
       e = hipEventRecord(p->join_ev[grp], p->gs[grp]);
       if (e == hipSuccess) e = hipStreamWaitEvent(stream, p->join_ev[grp], 0);
       if (e != hipSuccess) return hip_fail(e, "join of the group streams");
