@@ -216,6 +216,33 @@ def test_determinism_and_grouping():
             assert torch.equal(one.W[t][i], g1.W[t][i]) and torch.equal(one.M[t][i], g1.M[t][i])
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_later_work_on_the_stream_sees_the_whole_step(fused):
+    """Work enqueued on the caller's stream right after a step (no host
+    synchronisation) reads every matrix's final weights and momentum: the
+    first group runs on that stream, the second forks from it and joins back
+    (the staged plan); the fused plan runs there alone.  Both groups of
+    GPT-2 small, three steps in a row before the snapshot."""
+    say(f"[gpu] stream order after a step, fused={fused}")
+    from muon_newton_schulz_03_amd import MuonStep
+    wl = inputs.workload("gpt2_small")
+    dev = torch.device("cuda:0")
+    grads = [inputs.gradients("gpt2_small", t, device=dev) for t in range(3)]
+    W = [torch.zeros(s, device=dev) for s in wl.shapes]
+    M = [torch.zeros(s, device=dev) for s in wl.shapes]
+    plan = MuonStep(W, grads[0], M, fused=fused)
+    torch.cuda.synchronize()
+    for t in range(3):
+        plan.step(grads=grads[t], lr=wl.lr, momentum=wl.momentum)
+    snap_w = [w.clone() for w in W]  # same stream, queued behind the steps
+    snap_m = [m.clone() for m in M]
+    torch.cuda.synchronize()
+    for i in range(len(W)):
+        assert torch.equal(snap_w[i], W[i]) and torch.equal(snap_m[i], M[i]), f"matrix {i}"
+        assert torch.count_nonzero(W[i]).item() > 0, f"matrix {i} was not updated"
+    plan.close()
+
+
 def test_resume_equals_straight_run():
     say("[gpu] resume 2+2 == 4")
     from muon_newton_schulz_03_amd import MuonStep
