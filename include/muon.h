@@ -176,13 +176,15 @@ int muon_step_schedule(muon_plan* plan, const muon_matrix_desc* descs, int n, co
  * the process ends; the call allocates nothing.  It plans on the host each
  * time, copies the tables into that array from pageable host memory on
  * hip_stream (a later call first waits for that copy to have run) and
- * enqueues the step there (groups is ignored: one stream).
+ * enqueues the step there (groups and fused are ignored: one stream, three
+ * launches per iteration).
  * That copy is not meant for stream capture: capture the planned muon_step
  * instead.
  * Arguments are those of muon_init (opts: path, x_master_iters and max_T;
  * zero_momentum must be 0) and muon_step; the stream must belong to the
  * current device.  A set whose working memory exceeds the array fails with
- * MUON_E_WORKSPACE (muon_workspace_size gives the need, within a few KiB).
+ * MUON_E_WORKSPACE (muon_workspace_size with fused 0 gives the need, within a
+ * few KiB).
  * All calls on one GPU share its array and every call rewrites what it reads
  * before reading it, so only overlap matters: calls that can run at the same
  * time on one GPU (other streams, other host threads) race and must be
