@@ -198,3 +198,19 @@ def test_fused_step_in_a_graph():
     pe.close()
     pg.close()
     say("  replays equal to the eager fused plan")
+
+
+@pytest.mark.parametrize("name,nsteps,nesterov", [("illcond768", 1, True), ("aspect3072", 3, False),
+                                                  ("aspect3072", 3, True), ("width1024", 3, True)])
+def test_fused_matches_staged_on_the_other_workloads(name, nsteps, nesterov):
+    """The ill-conditioned, aspect-ratio and width-1024 workloads: the fused
+    plan's weights and momentum bitwise equal to the staged plan's after every
+    step (the width-1024 set places 144 matrices of three shapes on the XCDs)."""
+    say(f"[gpu] fused vs staged, {name}, {nsteps} steps, nesterov={nesterov}")
+    wl = inputs.workload(name)
+    steps = [inputs.gradients(name, t) for t in range(nsteps)]
+    kw = dict(T=5, momentum=wl.momentum, nesterov=nesterov, lr=wl.lr)
+    staged = run_plan(wl.shapes, steps, fused=False, **kw)
+    fused = run_plan(wl.shapes, steps, fused=True, **kw)
+    assert_bitwise(staged, fused, name)
+    say(f"  bitwise equal over {nsteps} steps, {len(wl.shapes)} matrices")
