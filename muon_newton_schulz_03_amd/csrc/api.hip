@@ -133,7 +133,7 @@ int check_desc(const muon_matrix_desc& d, int idx, bool need_ptrs) {
 struct Layout {
   // per matrix byte offsets into the workspace
   struct M {
-    size_t xlo, xo0, xo1, a, b, part, sc;
+    size_t xlo, xo0, xo1, a, b, bres, part, sc;
   };
   std::vector<M> m;
   size_t slots = 0, slot_bytes = 0;
@@ -430,6 +430,11 @@ size_t layout(const std::vector<Geometry>& geo, const Options& o, const Tables& 
     off = align_up(off + ae * es, kAlign);
     m.b = off;
     off = align_up(off + ae * es, kAlign);
+    m.bres = (size_t)-1;
+    if (!g.f32) {  // directly after B: the polynomial kernel stores it through B's buffer resource
+      m.bres = m.b + ae * es;
+      off = align_up(m.bres + sizeof(uint16_t) * g.mp, kAlign);
+    }
     m.part = off;
     off = align_up(off + sizeof(float) * g.nparts, kAlign);
     m.sc = off;

@@ -229,6 +229,44 @@ __device__ __forceinline__ Ctx ctx_of(const StageArgs& args, const Tile& tl) {
   return c;
 }
 
+// The residuals of B's diagonal, B_ii - bf16(B_ii) as bf16 words, follow B
+// directly in the workspace (2 mp bytes after its 2 mp mp).  Entry of row i:
+// a lane's rows i0 + 32 mi + l % 32 (mi = 0..3) of a 128-row panel at i0 are
+// four consecutive entries.
+__device__ __forceinline__ uint32_t bres_entry(uint32_t i) {
+  return 128u * (i >> 7) + 4u * (i & 31u) + ((i & 127u) >> 5);
+}
+
+// A tile's residuals for the rows a lane folds a*X into, rows R0 + 32 mi +
+// lane % 32 (mi = 0..3) of the wave's 128-row panel at R0, as four bf16
+// words.  Update kernels that read X's low bytes hold them in registers: one
+// 8-byte request per lane.  The others, short of registers in the weight
+// step, keep the panel's 128 words (256 bytes) in the unused low-byte buffers
+// instead, copied by one 4-byte-per-lane direct-to-LDS request, and read a
+// lane's four at each fold.  Either request moves nothing for an empty tile,
+// which still issues it so that the wait counts stay static.
+__device__ __forceinline__ rsrc_t res_rsrc(const Ctx& c) {
+  return make_rsrc(c.q, c.p ? c.qbytes + (c.qblk >> 7) : 0u);  // stage 3: c.q is B (c.qbytes = 2 mp mp), 2 mp = c.qblk / 128
+}
+__device__ __forceinline__ u32x2 issue_res_regs(const Ctx& c, int R0, int lane) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                       res_rsrc(c), c.qbytes + 2u * bres_entry((uint32_t)R0 + (uint32_t)(lane & 31)), 0, 0));
+}
+__device__ __forceinline__ void issue_res_lds(char* dst, const Ctx& c, int R0, int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(res_rsrc(c), MUON_LDS(dst), 4,
+                                           c.qbytes + 256u * (uint32_t)(R0 >> 7) + 4u * (uint32_t)lane, 0, 0, 0);
+}
+// The LDS copy: half `half` (tiles take the two 1 KiB halves of the first
+// low-byte buffer in turn, so that the next tile's can land while this tile's
+// are read), 256 bytes per wave; lane l's words at + 8 (l % 32).
+__device__ __forceinline__ char* res_lds(char* smem, int half, int w) { return smem + kLoBase + 1024 * half + 256 * w; }
+__device__ __forceinline__ u32x2 read_res(const char* src, int lane) { return *(const u32x2*)(src + 8 * (lane & 31)); }
+// Residual of block mi (0..3) of those rows.
+__device__ __forceinline__ float res_of(u32x2 r, int mi) {
+  const uint32_t w = mi < 2 ? r.x : r.y;
+  return __uint_as_float(mi & 1 ? w & 0xFFFF0000u : w << 16);
+}
+
 // Request slab kt of a tile into ring slot `slot` (kDma instructions per wave;
 // parts the tile does not need get empty resources, which move nothing).
 template <int STAGE>
@@ -459,6 +497,7 @@ struct Epi {
   int lane, t;
   float cb, cc, pre;
   void* out;     // stage 1: A; stage 2: B; stage 3: the new X
+  uint32_t resoff;  // stage 2: this lane's residual of a diagonal block at rows R0.. (byte offset from B; kOob for lanes >= 32)
   uint8_t* xlo;
   const void* ain;
   uint32_t mp, np;
@@ -483,6 +522,7 @@ struct Epi {
     }
     mp = (uint32_t)load_uniform(&m->mp);
     np = (uint32_t)load_uniform(&m->np);
+    resoff = lane < 32 ? mp * mp * 2u + 2u * bres_entry((uint32_t)(R0 + lane)) : kOob;
     xlo = nullptr;
     ain = nullptr;
     out = nullptr;
@@ -522,7 +562,7 @@ struct Epi {
     return 0;
   }
   __device__ __forceinline__ int stores_per_block() const {
-    if (STAGE != 3) return 6;
+    if (STAGE != 3) return 6;  // stage 2 issues one more (see process): counted as 6, waits only get stricter
     if (!kLastIt) return kLoOut ? 4 : 2;
     return w.fast ? 4 : 0;
   }
@@ -599,7 +639,8 @@ struct Epi {
     // stages 1 and 2: A or B, written at (i, j) and at (j, i)
     const int k = kind(b);
     if (k == kDiag) symmetrize(st, lane);
-    const rsrc_t o_rs = make_rsrc(out, mp * mp * 2u);
+    // stage 2 also covers the residuals of B's diagonal, stored right after B
+    const rsrc_t o_rs = make_rsrc(out, mp * mp * 2u + (STAGE == 2 ? mp * 2u : 0u));
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int r = rp_row(p, lane), c = rp_col(lane);
@@ -619,6 +660,19 @@ struct Epi {
       const uint32_t o = k != kLower ? (tiled(r0, c0, mp) + r * 32 + c) * 2u : kOob;
       store_b128(o_rs, o, pack8_bf16(v));
       if (STAGE == 2 || t == 1) write8(st, r, c, v);  // the mirrored writes take the final values
+    }
+    if (STAGE == 2) {
+      // B's diagonal went out as bf16 like every element; what the rounding
+      // left out, B_ii - bf16(B_ii), goes right after B (bres_entry order),
+      // for the update to add to its a*X coefficient.  The staged block now holds
+      // the final values: lane l < 32 takes element (l, l) of a diagonal
+      // block (row R0 + 32 (b / 2) + l: entry bres_entry(R0 + l) + b / 2).
+      // Every block issues the store (out of range elsewhere), and it is left
+      // out of the instruction counts the waits use: an uncounted request in
+      // flight only makes a wait stricter.
+      const float x = *st.elem(lane & 31, lane & 31);
+      const uint32_t doff = k == kDiag ? resoff + 2u * (uint32_t)(b >> 1) : kOob;
+      __builtin_amdgcn_raw_buffer_store_b16(f2bf(x - bf2f(f2bf(x))), o_rs, doff, 0, 0);
     }
     float blk[4][4];
     const int r = bp_row(lane), c = bp_col(lane);
@@ -666,12 +720,21 @@ struct Epi {
 
 // Requests of a tile's first slabs (and of its first low bytes) into ring
 // slots 0 .. kAhead - 1 and low-byte buffer 0: the start of a block's run of
-// tiles, with nothing of the ring in flight.
+// tiles, with nothing of the ring in flight.  Stage 3 first requests the
+// tile's residuals of B's diagonal (returned when held in registers; in LDS
+// half 0 otherwise).
 template <int STAGE, int MODE>
-__device__ __forceinline__ void tile_prologue(char* smem, const Ctx& c, int w, int lane) {
+__device__ __forceinline__ u32x2 tile_prologue(char* smem, const Ctx& c, int w, int wm, int lane) {
+  u32x2 res = {0u, 0u};
+  if (STAGE == 3 && (MODE & kHiLo)) res = issue_res_regs(c, c.i0 + 128 * wm, lane);
+  if (STAGE == 3 && !(MODE & kHiLo)) issue_res_lds(res_lds(smem, 0, w), c, c.i0 + 128 * wm, lane);
   if (STAGE == 3 && (MODE & kHiLo)) issue_lo(smem, c, 0, 0, w, lane);
 #pragma unroll
   for (int d = 0; d < Shape<STAGE>::kAhead; ++d) issue_slab<STAGE>(smem, c, d, d, w, lane);
+  // the register copy has landed once those are requested (the compiler sees
+  // the wait and adds none of its own where the residuals are used)
+  if (STAGE == 3 && (MODE & kHiLo)) MUON_WAIT_VMCNT(Shape<STAGE>::kAhead * Shape<STAGE>::kDma);
+  return res;
 }
 
 // One tile: its K loop, whose last slabs request the first slabs of the
@@ -679,12 +742,14 @@ __device__ __forceinline__ void tile_prologue(char* smem, const Ctx& c, int w, i
 // wait counts static), and its epilogue.  `g` counts the slabs the block has
 // consumed (ring slot g % kRing, low-byte buffer g % 2); `pend` is the number
 // of the previous epilogue's instructions issued after this tile's first
-// kAhead slabs.  Returns the instructions this tile's epilogue issued after
-// the next tile's first slabs.
+// kAhead slabs.  Stage 3: `res` and LDS half `half` hold the tile's residuals
+// of B's diagonal; the next tile's are requested into `resn` or the other
+// half, just before its second slab.  Returns the instructions this tile's
+// epilogue issued after the next tile's first slabs.
 template <int STAGE, int MODE>
 __device__ __forceinline__ int tile_pass(const StageArgs& args, char* smem, const Tile& tl, const Ctx& c,
                                          const Ctx& cn, int& g, int pend, int w, int wm, int wn, int lane,
-                                         const FragOff& fo) {
+                                         const FragOff& fo, u32x2 res, u32x2& resn, int half) {
   using E = Epi<STAGE, MODE>;
   using G = Shape<STAGE>;
   constexpr bool kLoIn = STAGE == 3 && (MODE & kHiLo);
@@ -737,6 +802,12 @@ __device__ __forceinline__ int tile_pass(const StageArgs& args, char* smem, cons
 #pragma unroll
       for (int b = 0; b < kDepth; ++b) ep.load(b, in[b % E::kInSlots]);
     }
+    if (STAGE == 3 && kt == nk - 1) {  // the next tile's residuals, before its second slab
+      if (kLoIn)
+        resn = issue_res_regs(cn, cn.i0 + 128 * wm, lane);
+      else
+        issue_res_lds(res_lds(smem, half ^ 1, w), cn, cn.i0 + 128 * wm, lane);
+    }
     const int slot = (g + kAhead) % G::kRing;
     if (kt + kAhead < nk)
       issue_slab<STAGE>(smem, c, kt + kAhead, slot, w, lane);
@@ -750,11 +821,12 @@ __device__ __forceinline__ int tile_pass(const StageArgs& args, char* smem, cons
         const int rel = kt * kBK - R0;  // this slab's K rows are output rows of the wave
         if (rel >= 0 && rel < 128) {
           const char* lo = smem + kLoBase + (g & 1) * kLoBuf;
+          const float al = alpha + res_of(kLoIn ? res : read_res(res_lds(smem, half, w), lane), rel >> 5);
           switch (rel >> 5) {
-            case 0: fold_x<kLoIn>(acc[0], p, lo, wn, lane, alpha); break;
-            case 1: fold_x<kLoIn>(acc[1], p, lo, wn, lane, alpha); break;
-            case 2: fold_x<kLoIn>(acc[2 % G::kMI], p, lo, wn, lane, alpha); break;
-            default: fold_x<kLoIn>(acc[3 % G::kMI], p, lo, wn, lane, alpha); break;
+            case 0: fold_x<kLoIn>(acc[0], p, lo, wn, lane, al); break;
+            case 1: fold_x<kLoIn>(acc[1], p, lo, wn, lane, al); break;
+            case 2: fold_x<kLoIn>(acc[2 % G::kMI], p, lo, wn, lane, al); break;
+            default: fold_x<kLoIn>(acc[3 % G::kMI], p, lo, wn, lane, al); break;
           }
         }
         mma_slab<true, G::kMI>(acc, s + wm * kHalf, p, wn, lane, fo);
@@ -808,9 +880,21 @@ __global__ __launch_bounds__(kThreads, kBlocks) void ns_bf16_kernel(StageArgs ar
   if (q >= args.ntiles) return;
   Tile tl = tile_of(raw);
   Ctx c = ctx_of<STAGE, MODE>(args, tl);
+  // stage 3: the residuals of B's diagonal for the rows this lane folds a*X
+  // into (issue_res_regs, issue_res_lds): the first tile's requested here,
+  // each next tile's just before its second slab, so that the wait for its
+  // first slab covers them.  res, resn: this tile's and the next one's when
+  // held in registers; LDS half `half` otherwise.
+  u32x2 res = {0u, 0u}, resn = res;
+  int half = 0;
+  if (STAGE == 3 && kLoIn) res = issue_res_regs(c, c.i0 + 128 * wm, lane);
+  if (STAGE == 3 && !kLoIn) issue_res_lds(res_lds(smem, 0, w), c, c.i0 + 128 * wm, lane);
   if (kLoIn) issue_lo(smem, c, 0, 0, w, lane);
 #pragma unroll
   for (int d = 0; d < kAhead; ++d) issue_slab<STAGE>(smem, c, d, d, w, lane);
+  // the register copy has landed once those are requested (the compiler sees
+  // the wait and adds none of its own where the residuals are used)
+  if (STAGE == 3 && kLoIn) MUON_WAIT_VMCNT(kAhead * kD);
   int g = 0;     // slabs consumed by this block so far (ring slot g % kRing, low-byte buffer g % 2)
   int pend = 0;  // the previous epilogue's instructions, issued after this tile's first kAhead slabs
   for (;;) {
@@ -870,6 +954,12 @@ __global__ __launch_bounds__(kThreads, kBlocks) void ns_bf16_kernel(StageArgs ar
 #pragma unroll
         for (int b = 0; b < kDepth; ++b) ep.load(b, in[b % E::kInSlots]);
       }
+      if (STAGE == 3 && kt == nk - 1) {  // the next tile's residuals, before its second slab
+        if (kLoIn)
+          resn = issue_res_regs(cn, cn.i0 + 128 * wm, lane);
+        else
+          issue_res_lds(res_lds(smem, half ^ 1, w), cn, cn.i0 + 128 * wm, lane);
+      }
       const int slot = (g + kAhead) % G::kRing;
       if (kt + kAhead < nk)
         issue_slab<STAGE>(smem, c, kt + kAhead, slot, w, lane);
@@ -883,11 +973,12 @@ __global__ __launch_bounds__(kThreads, kBlocks) void ns_bf16_kernel(StageArgs ar
           const int rel = kt * kBK - R0;  // this slab's K rows are output rows of the wave
           if (rel >= 0 && rel < 128) {
             const char* lo = smem + kLoBase + (g & 1) * kLoBuf;
+            const float al = alpha + res_of(kLoIn ? res : read_res(res_lds(smem, half, w), lane), rel >> 5);
             switch (rel >> 5) {
-              case 0: fold_x<kLoIn>(acc[0], p, lo, wn, lane, alpha); break;
-              case 1: fold_x<kLoIn>(acc[1], p, lo, wn, lane, alpha); break;
-              case 2: fold_x<kLoIn>(acc[2 % G::kMI], p, lo, wn, lane, alpha); break;
-              default: fold_x<kLoIn>(acc[3 % G::kMI], p, lo, wn, lane, alpha); break;
+              case 0: fold_x<kLoIn>(acc[0], p, lo, wn, lane, al); break;
+              case 1: fold_x<kLoIn>(acc[1], p, lo, wn, lane, al); break;
+              case 2: fold_x<kLoIn>(acc[2 % G::kMI], p, lo, wn, lane, al); break;
+              default: fold_x<kLoIn>(acc[3 % G::kMI], p, lo, wn, lane, al); break;
             }
           }
           mma_slab<true, G::kMI>(acc, s + wm * kHalf, p, wn, lane, fo);
@@ -918,6 +1009,8 @@ __global__ __launch_bounds__(kThreads, kBlocks) void ns_bf16_kernel(StageArgs ar
     q = qn;
     tl = tn;
     c = cn;
+    res = resn;
+    half ^= 1;
   }
 }
 
@@ -973,9 +1066,10 @@ __device__ __forceinline__ void fused_tile(const StageArgs& args, char* smem, co
   const Ctx c = ctx_of<STAGE, MODE>(args, tl);
   Ctx cn = c;
   cn.p = nullptr;  // no next tile: empty requests
-  tile_prologue<STAGE, MODE>(smem, c, w, lane);
+  const u32x2 res = tile_prologue<STAGE, MODE>(smem, c, w, wm, lane);
+  u32x2 resn;
   int g = 0;
-  (void)tile_pass<STAGE, MODE>(args, smem, tl, c, cn, g, 0, w, wm, wn, lane, fo);
+  (void)tile_pass<STAGE, MODE>(args, smem, tl, c, cn, g, 0, w, wm, wn, lane, fo, res, resn, 0);
   MUON_WAIT_VMCNT(0);
 }
 

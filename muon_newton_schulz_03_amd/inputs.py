@@ -173,6 +173,20 @@ def gradients(name: str, step: int, run: int = 0, device="cpu",
     return out
 
 
+def orthonormal_rows(rows: int, cols: int, seed: int, scale: float = 0.02,
+                     dtype=torch.bfloat16) -> torch.Tensor:
+    """scale * Q with orthonormal rows or columns (QR of a seeded Gaussian, built
+    in fp64 on the CPU), rows x cols: every singular value equal to ``scale``
+    before the rounding to ``dtype``.  A flat spectrum is the degenerate case
+    of the iteration in which all singular values take the same path."""
+    m, n = min(rows, cols), max(rows, cols)
+    g = _gen(_SEED_BASE["custom"] + 7919 * seed, "cpu")
+    q, r = torch.linalg.qr(torch.randn(n, m, generator=g, dtype=torch.float64))
+    q = q * torch.sign(torch.diagonal(r)).unsqueeze(0)  # n x m, orthonormal columns
+    x = q.T if rows <= cols else q
+    return (scale * x).contiguous().to(dtype)
+
+
 def custom_gradient(rows: int, cols: int, seed: int, dtype=torch.bfloat16, std: float = 1.0,
                     device="cpu") -> torch.Tensor:
     """One std*N(0,1) matrix of an arbitrary shape (ragged and edge-case tests)."""

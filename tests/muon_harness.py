@@ -111,6 +111,51 @@ def update_from_weights(w_after, w_before, lr, scale=1.0):
     return (np.asarray(w_before, np.float64) - np.asarray(w_after, np.float64)) / (O.f32(lr) * scale)
 
 
+def compare_run(shapes, grads_steps, gpu, *, path, lr, mu, nesterov, T=5, coeffs=(A, B, C), w0=None,
+                scales=None, sample=None, steps=None, tol=None, schedule=None):
+    tol = tol if tol is not None else (TOL_F32 if path == "f32" else TOL_BF16)
+    sample = list(range(len(shapes))) if sample is None else list(sample)
+    worst = 0.0
+    for si, i in enumerate(sample):
+        wi0 = w0[i] if w0 is not None else torch.zeros(shapes[i])
+        s = 1.0 if scales is None or scales[i] <= 0 else O.f32(scales[i])
+        ref = oracle_steps(wi0, [g[i] for g in grads_steps], T=T, mu=mu, nesterov=nesterov, lr=lr,
+                           coeffs=coeffs, scale=s, schedule=schedule)
+        prev = O.as_f64(wi0)
+        for t, r in enumerate(ref):
+            if gpu.W[t] is None or (t > 0 and gpu.W[t - 1] is None):
+                continue
+            og = update_from_weights(gpu.W[t][si], prev if t == 0 else gpu.W[t - 1][si], lr, s)
+            e = O.rel_frobenius(og, r.O)
+            worst = max(worst, e)
+            assert e <= tol, f"matrix {i} {shapes[i]} step {t}: rel err {e:.3e} > {tol}"
+            check_momentum(gpu.M[t][si], r.M, f"matrix {i} step {t}")
+    return worst
+
+
+def ns_gram_factor(A0: np.ndarray, a: float, b: float, c: float, T: int) -> np.ndarray:
+    """Q with X_T = Q X_0 after T quintic Newton-Schulz steps, from A0 = X_0 X_0^T alone.
+
+    Each step multiplies X on the left by a polynomial in A_t = X_t X_t^T, and
+    every A_t is a polynomial in A0, so all of them share A0's eigenvectors V.
+    An eigenvalue s^2 of A0 belongs to a singular value s of X_0, which one step
+    maps to s (a + b s^2 + c s^4); hence Q = V diag(prod_t (a + b s_t^2 +
+    c s_t^4)) V^T.  This is the SVD closed form the oracle's pins use, reached
+    through the m x m Gram matrix, so a reference for X_T costs one pass over
+    X_0 whatever its column count.  Coefficients are rounded to fp32 as the
+    oracle and the C ABI round them.
+    """
+    a, b, c = O.f32(a), O.f32(b), O.f32(c)
+    lam, V = np.linalg.eigh(np.asarray(A0, np.float64))
+    s = np.sqrt(np.clip(lam, 0.0, None))
+    g = np.ones_like(s)
+    for _ in range(T):
+        p = a + b * s * s + c * s ** 4
+        g *= p
+        s = s * p
+    return (V * g) @ V.T
+
+
 @dataclass
 class StreamResult:
     worst: Dict[int, float] = field(default_factory=dict)       # worst rel err of O per compared matrix

@@ -65,10 +65,11 @@ def test_workspace_size_model(lib):
     # no low bytes: 1 byte per element less
     ws0 = lib.muon_workspace_size(arr, 1, ctypes.byref(Options(0, 0, 0, 0)))
     assert ws - ws0 == x
-    # fp32 path: 4-byte operands, no master; its 128 x 128 tile tables are longer
-    # than the bf16 path's 256 x 128 ones (a few 256-byte blocks)
+    # fp32 path: 4-byte operands, no master and no residuals of B's diagonal (2
+    # bytes per row on the bf16 path); its 128 x 128 tile tables are longer than
+    # the bf16 path's 256 x 128 ones (a few 256-byte blocks)
     wsf = lib.muon_workspace_size(arr, 1, ctypes.byref(Options(1, -1, 0, 0)))
-    assert 0 <= wsf - ws0 - 4 * x * 2 < 4096
+    assert 0 <= wsf - (ws0 - 2 * 768) - 4 * x * 2 < 4096
     g = inputs.workload("gpt2_small")
     d, _ = describe(g.shapes)
     assert 0.59e9 < d["workspace_bytes"] < 0.60e9
@@ -266,6 +267,25 @@ def test_validation_errors(lib):
     expect_error(E.MUON_E_INVAL, lib.muon_init, ok, 1, None, ws, 1 << 30, None, None)
     assert not plan.value
     assert lib.muon_workspace_size(bad, 1, None) == 0
+
+
+def test_size_limits(lib):
+    """Sides up to 2^20 and buffers below 2 GiB are accepted (the largest
+    shapes the GPU limit tests run); one element more on a side, or a padded
+    buffer of 2 GiB, is refused before anything is allocated."""
+    for shape in [(128, 1 << 20), (1 << 20, 128), (100, (1 << 20) - 1), (512, 1048447), (1024, 524160),
+                  (23040, 23040)]:
+        ws = lib.muon_workspace_size(descs([shape]), 1, None)
+        assert ws > 0, (shape, _lib.last_error())
+    for shape, why in [((128, (1 << 20) + 1), "limit per side"), (((1 << 20) + 1, 1), "limit per side"),
+                       ((1024, 524289), "2 GiB"), ((23296, 23296), "2 GiB"), ((512, 1048577), "limit per side")]:
+        assert lib.muon_workspace_size(descs([shape]), 1, None) == 0, shape
+        assert why in _lib.last_error(), (shape, _lib.last_error())
+    # the tile tables index tiles with 16 bits: the longest side's lists still cover every tile
+    d, t = describe([(512, 1048447)], kind=_lib.KIND_UPDATE)
+    assert len([x for x in t if x[0] >= 0]) == 2 * 8191
+    d, t = describe([(512, 1048447)], kind=_lib.KIND_MOMENTUM)
+    assert len([x for x in t if x[0] >= 0]) == 8 * 16382
 
 
 def test_step_and_destroy_on_null_plan(lib):

@@ -62,3 +62,14 @@ def test_weights(seed):
     w = inputs.weights([(3, 4), (5, 2)], seed)
     assert [t.shape for t in w] == [(3, 4), (5, 2)]
     assert (seed is None) == all(not t.any() for t in w)
+
+
+def test_orthonormal_rows_have_a_flat_spectrum():
+    for shape in [(64, 300), (300, 64), (50, 50)]:
+        x = inputs.orthonormal_rows(*shape, seed=3, scale=0.5)
+        assert x.shape == shape and x.dtype == torch.bfloat16
+        sv = torch.linalg.svdvals(x.double())
+        assert float(sv.max() / sv.min()) < 1.02  # bf16 rounding only
+        assert abs(float(sv.mean()) - 0.5) < 5e-3
+    assert torch.equal(inputs.orthonormal_rows(64, 300, 3), inputs.orthonormal_rows(64, 300, 3))
+    assert not torch.equal(inputs.orthonormal_rows(64, 300, 3), inputs.orthonormal_rows(64, 300, 4))
