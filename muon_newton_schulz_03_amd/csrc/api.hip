@@ -428,13 +428,11 @@ size_t layout(const std::vector<Geometry>& geo, const Options& o, const Tables& 
     off = align_up(off + xe * es, kAlign);
     m.a = off;
     off = align_up(off + ae * es, kAlign);
+    // bf16 path: B is followed directly by mp fp32 words, what B's stored
+    // diagonal lacks (the kernels reach them through B's buffer resource)
     m.b = off;
-    off = align_up(off + ae * es, kAlign);
-    m.bres = (size_t)-1;
-    if (!g.f32) {  // directly after B: the polynomial kernel stores it through B's buffer resource
-      m.bres = m.b + ae * es;
-      off = align_up(m.bres + sizeof(uint16_t) * g.mp, kAlign);
-    }
+    off = align_up(off + ae * es + (g.f32 ? 0 : sizeof(float) * g.mp), kAlign);
+    m.bres = g.f32 ? (size_t)-1 : m.b + ae * es;
     m.part = off;
     off = align_up(off + sizeof(float) * g.nparts, kAlign);
     m.sc = off;

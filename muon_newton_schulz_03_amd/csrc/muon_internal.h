@@ -35,8 +35,10 @@ struct DevMat {
   uint8_t* xlo;       // bf16 path: low byte of X (the rounded fp32-pattern distance to bf16(X) / 256, mp x np); else null
   void* xo[2];        // operand copies of X (ping-pong), bf16 or f32, mp x np
   void* a;            // A = X X^T, mp x mp (bf16 or f32)
-  void* b;            // B = b A + c A A, mp x mp; on the bf16 path followed directly by B_ii - bf16(B_ii)
-                      // for each row i, as bf16 (the rounding left out of B's stored diagonal)
+  void* b;            // B = b A + c A A, mp x mp; on the bf16 path followed directly by mp fp32 words,
+                      // for each row i what B's stored diagonal lacks: the change of B_ii that the
+                      // rounding of A_ii causes (stored by the Gram kernel), plus B_ii - bf16(B_ii)
+                      // (added by the polynomial kernel)
   float* part;        // momentum-kernel partial sums of squares, one per tile
   float* sc;          // [0] = 1/(||U||_F + eps), [1] = ||U||_F
   int32_t rows, cols; // original shape

@@ -229,42 +229,46 @@ __device__ __forceinline__ Ctx ctx_of(const StageArgs& args, const Tile& tl) {
   return c;
 }
 
-// The residuals of B's diagonal, B_ii - bf16(B_ii) as bf16 words, follow B
-// directly in the workspace (2 mp bytes after its 2 mp mp).  Entry of row i:
-// a lane's rows i0 + 32 mi + l % 32 (mi = 0..3) of a 128-row panel at i0 are
-// four consecutive entries.
+// What B's stored diagonal lacks, per row i: the change of B_ii that the
+// rounding of A_ii causes (the Gram epilogue stores it) plus B_ii - bf16(B_ii)
+// (the polynomial epilogue adds it), as fp32 words right after B (4 mp bytes
+// after its 2 mp mp).  Entry of row i: a lane's rows i0 + 32 mi + l % 32 (mi =
+// 0..3) of a 128-row panel at i0 are four consecutive entries.
 __device__ __forceinline__ uint32_t bres_entry(uint32_t i) {
   return 128u * (i >> 7) + 4u * (i & 31u) + ((i & 127u) >> 5);
 }
 
-// A tile's residuals for the rows a lane folds a*X into, rows R0 + 32 mi +
-// lane % 32 (mi = 0..3) of the wave's 128-row panel at R0, as four bf16
-// words.  Update kernels that read X's low bytes hold them in registers: one
-// 8-byte request per lane.  The others, short of registers in the weight
-// step, keep the panel's 128 words (256 bytes) in the unused low-byte buffers
-// instead, copied by one 4-byte-per-lane direct-to-LDS request, and read a
-// lane's four at each fold.  Either request moves nothing for an empty tile,
+// A tile's diagonal words for the rows a lane folds a*X into, rows R0 + 32 mi
+// + lane % 32 (mi = 0..3) of the wave's 128-row panel at R0.  Update kernels
+// that read X's low bytes hold them in registers: one 16-byte request per
+// lane.  The others, short of registers in the weight step, keep the panel's
+// 512 bytes in the unused low-byte buffers instead, copied by two 4-byte
+// direct-to-LDS requests per lane, and read a lane's word at each fold.  Either request moves nothing for an empty tile,
 // which still issues it so that the wait counts stay static.
 __device__ __forceinline__ rsrc_t res_rsrc(const Ctx& c) {
-  return make_rsrc(c.q, c.p ? c.qbytes + (c.qblk >> 7) : 0u);  // stage 3: c.q is B (c.qbytes = 2 mp mp), 2 mp = c.qblk / 128
+  return make_rsrc(c.q, c.p ? c.qbytes + (c.qblk >> 6) : 0u);  // stage 3: c.q is B (c.qbytes = 2 mp mp), 4 mp = c.qblk / 64
 }
-__device__ __forceinline__ u32x2 issue_res_regs(const Ctx& c, int R0, int lane) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                       res_rsrc(c), c.qbytes + 2u * bres_entry((uint32_t)R0 + (uint32_t)(lane & 31)), 0, 0));
+__device__ __forceinline__ u32x4 issue_res_regs(const Ctx& c, int R0, int lane) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       res_rsrc(c), c.qbytes + 4u * bres_entry((uint32_t)R0 + (uint32_t)(lane & 31)), 0, 0));
 }
 __device__ __forceinline__ void issue_res_lds(char* dst, const Ctx& c, int R0, int lane) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(res_rsrc(c), MUON_LDS(dst), 4,
-                                           c.qbytes + 256u * (uint32_t)(R0 >> 7) + 4u * (uint32_t)lane, 0, 0, 0);
+  const rsrc_t rs = res_rsrc(c);
+  const uint32_t off = c.qbytes + 512u * (uint32_t)(R0 >> 7) + 4u * (uint32_t)lane;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MUON_LDS(dst + 256 * h), 4, off + 256u * h, 0, 0, 0);
 }
-// The LDS copy: half `half` (tiles take the two 1 KiB halves of the first
-// low-byte buffer in turn, so that the next tile's can land while this tile's
-// are read), 256 bytes per wave; lane l's words at + 8 (l % 32).
-__device__ __forceinline__ char* res_lds(char* smem, int half, int w) { return smem + kLoBase + 1024 * half + 256 * w; }
-__device__ __forceinline__ u32x2 read_res(const char* src, int lane) { return *(const u32x2*)(src + 8 * (lane & 31)); }
-// Residual of block mi (0..3) of those rows.
-__device__ __forceinline__ float res_of(u32x2 r, int mi) {
-  const uint32_t w = mi < 2 ? r.x : r.y;
-  return __uint_as_float(mi & 1 ? w & 0xFFFF0000u : w << 16);
+// The LDS copy: half `half` (tiles take the two low-byte buffers in turn, so
+// that the next tile's words can land while this tile's are read), 1 KiB per
+// wave; lane l's word of block mi at + 16 (l % 32) + 4 mi.
+__device__ __forceinline__ char* res_lds(char* smem, int half, int w) { return smem + kLoBase + kLoBuf * half + 1024 * w; }
+__device__ __forceinline__ float read_res(const char* src, int lane, int mi) {
+  return *(const float*)(src + 16 * (lane & 31) + 4 * mi);
+}
+// Word of block mi (0..3) of those rows.
+__device__ __forceinline__ float res_of(u32x4 r, int mi) {
+  const uint32_t lo = mi & 1 ? r.y : r.x, hi = mi & 1 ? r.w : r.z;
+  return __uint_as_float(mi < 2 ? lo : hi);
 }
 
 // Request slab kt of a tile into ring slot `slot` (kDma instructions per wave;
@@ -496,8 +500,11 @@ struct Epi {
   int R0, C0;    // the wave's canonical origin
   int lane, t;
   float cb, cc, pre;
+  float dbs;     // stage 1: the factor of the polynomial's b and c (s at t = 1, else 1)
+  void* bmat;    // stage 1: B, whose diagonal words the Gram epilogue stores
   void* out;     // stage 1: A; stage 2: B; stage 3: the new X
-  uint32_t resoff;  // stage 2: this lane's residual of a diagonal block at rows R0.. (byte offset from B; kOob for lanes >= 32)
+  uint32_t resoff;  // stages 1, 2: this lane's diagonal word for a diagonal block at rows R0.. (byte offset
+                    // from B; kOob for lanes >= 32)
   uint8_t* xlo;
   const void* ain;
   uint32_t mp, np;
@@ -515,14 +522,16 @@ struct Epi {
     cb = args.b;
     cc = args.c;
     pre = 1.f;
+    dbs = 1.f;
     if (args.t == 1 && STAGE != 3) {  // the first iteration works on U = X0 / s (s = 1 / (||U|| + eps))
       const float s = load_uniform(load_uniform(&m->sc));
-      if (STAGE == 1) pre = s * s;
+      if (STAGE == 1) pre = s * s, dbs = s;
       if (STAGE == 2) cb *= s, cc *= s;
     }
     mp = (uint32_t)load_uniform(&m->mp);
     np = (uint32_t)load_uniform(&m->np);
-    resoff = lane < 32 ? mp * mp * 2u + 2u * bres_entry((uint32_t)(R0 + lane)) : kOob;
+    resoff = lane < 32 ? mp * mp * 2u + 4u * bres_entry((uint32_t)(R0 + lane)) : kOob;
+    bmat = STAGE == 1 ? load_uniform(&m->b) : nullptr;
     xlo = nullptr;
     ain = nullptr;
     out = nullptr;
@@ -639,8 +648,7 @@ struct Epi {
     // stages 1 and 2: A or B, written at (i, j) and at (j, i)
     const int k = kind(b);
     if (k == kDiag) symmetrize(st, lane);
-    // stage 2 also covers the residuals of B's diagonal, stored right after B
-    const rsrc_t o_rs = make_rsrc(out, mp * mp * 2u + (STAGE == 2 ? mp * 2u : 0u));
+    const rsrc_t o_rs = make_rsrc(out, mp * mp * 2u);
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int r = rp_row(p, lane), c = rp_col(lane);
@@ -661,18 +669,26 @@ struct Epi {
       store_b128(o_rs, o, pack8_bf16(v));
       if (STAGE == 2 || t == 1) write8(st, r, c, v);  // the mirrored writes take the final values
     }
-    if (STAGE == 2) {
-      // B's diagonal went out as bf16 like every element; what the rounding
-      // left out, B_ii - bf16(B_ii), goes right after B (bres_entry order),
-      // for the update to add to its a*X coefficient.  The staged block now holds
-      // the final values: lane l < 32 takes element (l, l) of a diagonal
-      // block (row R0 + 32 (b / 2) + l: entry bres_entry(R0 + l) + b / 2).
-      // Every block issues the store (out of range elsewhere), and it is left
-      // out of the instruction counts the waits use: an uncounted request in
-      // flight only makes a wait stricter.
+    {
+      // The diagonal went out as bf16 like every element.  The staged block
+      // now holds the final values: lane l < 32 takes element (l, l) of a
+      // diagonal block (row R0 + 32 (b / 2) + l: entry bres_entry(R0 + l) +
+      // b / 2), and r = x - bf16(x) is what the rounding left out.  Into B's
+      // diagonal word of that row:
+      //   stage 1 stores the change of B_ii that r causes, (b + 2 c A_ii) r,
+      //     with the polynomial's b and c (both times s at t = 1);
+      //   stage 2 adds r (an atomic add, which returns nothing to wait for).
+      // Every block issues the request (out of range elsewhere), and it is
+      // left out of the instruction counts the waits use: an uncounted
+      // request in flight only makes a wait stricter.
       const float x = *st.elem(lane & 31, lane & 31);
-      const uint32_t doff = k == kDiag ? resoff + 2u * (uint32_t)(b >> 1) : kOob;
-      __builtin_amdgcn_raw_buffer_store_b16(f2bf(x - bf2f(f2bf(x))), o_rs, doff, 0, 0);
+      const float r = x - bf2f(f2bf(x));
+      const uint32_t doff = k == kDiag ? resoff + 4u * (uint32_t)(b >> 1) : kOob;
+      const rsrc_t w_rs = make_rsrc(STAGE == 1 ? bmat : out, mp * mp * 2u + mp * 4u);
+      if (STAGE == 1)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dbs * fmaf(2.f * cc, x, cb) * r), w_rs, doff, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(r, w_rs, doff, 0, 0);
     }
     float blk[4][4];
     const int r = bp_row(lane), c = bp_col(lane);
@@ -721,18 +737,18 @@ struct Epi {
 // Requests of a tile's first slabs (and of its first low bytes) into ring
 // slots 0 .. kAhead - 1 and low-byte buffer 0: the start of a block's run of
 // tiles, with nothing of the ring in flight.  Stage 3 first requests the
-// tile's residuals of B's diagonal (returned when held in registers; in LDS
-// half 0 otherwise).
+// tile's diagonal words of B (returned when held in registers; in LDS half 0
+// otherwise).
 template <int STAGE, int MODE>
-__device__ __forceinline__ u32x2 tile_prologue(char* smem, const Ctx& c, int w, int wm, int lane) {
-  u32x2 res = {0u, 0u};
+__device__ __forceinline__ u32x4 tile_prologue(char* smem, const Ctx& c, int w, int wm, int lane) {
+  u32x4 res = {0u, 0u, 0u, 0u};
   if (STAGE == 3 && (MODE & kHiLo)) res = issue_res_regs(c, c.i0 + 128 * wm, lane);
   if (STAGE == 3 && !(MODE & kHiLo)) issue_res_lds(res_lds(smem, 0, w), c, c.i0 + 128 * wm, lane);
   if (STAGE == 3 && (MODE & kHiLo)) issue_lo(smem, c, 0, 0, w, lane);
 #pragma unroll
   for (int d = 0; d < Shape<STAGE>::kAhead; ++d) issue_slab<STAGE>(smem, c, d, d, w, lane);
   // the register copy has landed once those are requested (the compiler sees
-  // the wait and adds none of its own where the residuals are used)
+  // the wait and adds none of its own where the words are used)
   if (STAGE == 3 && (MODE & kHiLo)) MUON_WAIT_VMCNT(Shape<STAGE>::kAhead * Shape<STAGE>::kDma);
   return res;
 }
@@ -742,14 +758,14 @@ __device__ __forceinline__ u32x2 tile_prologue(char* smem, const Ctx& c, int w, 
 // wait counts static), and its epilogue.  `g` counts the slabs the block has
 // consumed (ring slot g % kRing, low-byte buffer g % 2); `pend` is the number
 // of the previous epilogue's instructions issued after this tile's first
-// kAhead slabs.  Stage 3: `res` and LDS half `half` hold the tile's residuals
-// of B's diagonal; the next tile's are requested into `resn` or the other
+// kAhead slabs.  Stage 3: `res` and LDS half `half` hold the tile's diagonal
+// words of B; the next tile's are requested into `resn` or the other
 // half, just before its second slab.  Returns the instructions this tile's
 // epilogue issued after the next tile's first slabs.
 template <int STAGE, int MODE>
 __device__ __forceinline__ int tile_pass(const StageArgs& args, char* smem, const Tile& tl, const Ctx& c,
                                          const Ctx& cn, int& g, int pend, int w, int wm, int wn, int lane,
-                                         const FragOff& fo, u32x2 res, u32x2& resn, int half) {
+                                         const FragOff& fo, u32x4 res, u32x4& resn, int half) {
   using E = Epi<STAGE, MODE>;
   using G = Shape<STAGE>;
   constexpr bool kLoIn = STAGE == 3 && (MODE & kHiLo);
@@ -802,7 +818,7 @@ __device__ __forceinline__ int tile_pass(const StageArgs& args, char* smem, cons
 #pragma unroll
       for (int b = 0; b < kDepth; ++b) ep.load(b, in[b % E::kInSlots]);
     }
-    if (STAGE == 3 && kt == nk - 1) {  // the next tile's residuals, before its second slab
+    if (STAGE == 3 && kt == nk - 1) {  // the next tile's diagonal words, before its second slab
       if (kLoIn)
         resn = issue_res_regs(cn, cn.i0 + 128 * wm, lane);
       else
@@ -821,7 +837,7 @@ __device__ __forceinline__ int tile_pass(const StageArgs& args, char* smem, cons
         const int rel = kt * kBK - R0;  // this slab's K rows are output rows of the wave
         if (rel >= 0 && rel < 128) {
           const char* lo = smem + kLoBase + (g & 1) * kLoBuf;
-          const float al = alpha + res_of(kLoIn ? res : read_res(res_lds(smem, half, w), lane), rel >> 5);
+          const float al = alpha + (kLoIn ? res_of(res, rel >> 5) : read_res(res_lds(smem, half, w), lane, rel >> 5));
           switch (rel >> 5) {
             case 0: fold_x<kLoIn>(acc[0], p, lo, wn, lane, al); break;
             case 1: fold_x<kLoIn>(acc[1], p, lo, wn, lane, al); break;
@@ -880,12 +896,12 @@ __global__ __launch_bounds__(kThreads, kBlocks) void ns_bf16_kernel(StageArgs ar
   if (q >= args.ntiles) return;
   Tile tl = tile_of(raw);
   Ctx c = ctx_of<STAGE, MODE>(args, tl);
-  // stage 3: the residuals of B's diagonal for the rows this lane folds a*X
-  // into (issue_res_regs, issue_res_lds): the first tile's requested here,
-  // each next tile's just before its second slab, so that the wait for its
-  // first slab covers them.  res, resn: this tile's and the next one's when
-  // held in registers; LDS half `half` otherwise.
-  u32x2 res = {0u, 0u}, resn = res;
+  // stage 3: B's diagonal words (what its stored diagonal lacks) for the rows
+  // this lane folds a*X into (issue_res_regs, issue_res_lds): the first
+  // tile's requested here, each next tile's just before its second slab, so
+  // that the wait for its first slab covers them.  res, resn: this tile's and
+  // the next one's when held in registers; LDS half `half` otherwise.
+  u32x4 res = {0u, 0u, 0u, 0u}, resn = res;
   int half = 0;
   if (STAGE == 3 && kLoIn) res = issue_res_regs(c, c.i0 + 128 * wm, lane);
   if (STAGE == 3 && !kLoIn) issue_res_lds(res_lds(smem, 0, w), c, c.i0 + 128 * wm, lane);
@@ -893,7 +909,7 @@ __global__ __launch_bounds__(kThreads, kBlocks) void ns_bf16_kernel(StageArgs ar
 #pragma unroll
   for (int d = 0; d < kAhead; ++d) issue_slab<STAGE>(smem, c, d, d, w, lane);
   // the register copy has landed once those are requested (the compiler sees
-  // the wait and adds none of its own where the residuals are used)
+  // the wait and adds none of its own where the words are used)
   if (STAGE == 3 && kLoIn) MUON_WAIT_VMCNT(kAhead * kD);
   int g = 0;     // slabs consumed by this block so far (ring slot g % kRing, low-byte buffer g % 2)
   int pend = 0;  // the previous epilogue's instructions, issued after this tile's first kAhead slabs
@@ -954,7 +970,7 @@ __global__ __launch_bounds__(kThreads, kBlocks) void ns_bf16_kernel(StageArgs ar
 #pragma unroll
         for (int b = 0; b < kDepth; ++b) ep.load(b, in[b % E::kInSlots]);
       }
-      if (STAGE == 3 && kt == nk - 1) {  // the next tile's residuals, before its second slab
+      if (STAGE == 3 && kt == nk - 1) {  // the next tile's diagonal words, before its second slab
         if (kLoIn)
           resn = issue_res_regs(cn, cn.i0 + 128 * wm, lane);
         else
@@ -973,7 +989,7 @@ __global__ __launch_bounds__(kThreads, kBlocks) void ns_bf16_kernel(StageArgs ar
           const int rel = kt * kBK - R0;  // this slab's K rows are output rows of the wave
           if (rel >= 0 && rel < 128) {
             const char* lo = smem + kLoBase + (g & 1) * kLoBuf;
-            const float al = alpha + res_of(kLoIn ? res : read_res(res_lds(smem, half, w), lane), rel >> 5);
+            const float al = alpha + (kLoIn ? res_of(res, rel >> 5) : read_res(res_lds(smem, half, w), lane, rel >> 5));
             switch (rel >> 5) {
               case 0: fold_x<kLoIn>(acc[0], p, lo, wn, lane, al); break;
               case 1: fold_x<kLoIn>(acc[1], p, lo, wn, lane, al); break;
@@ -1066,8 +1082,8 @@ __device__ __forceinline__ void fused_tile(const StageArgs& args, char* smem, co
   const Ctx c = ctx_of<STAGE, MODE>(args, tl);
   Ctx cn = c;
   cn.p = nullptr;  // no next tile: empty requests
-  const u32x2 res = tile_prologue<STAGE, MODE>(smem, c, w, wm, lane);
-  u32x2 resn;
+  const u32x4 res = tile_prologue<STAGE, MODE>(smem, c, w, wm, lane);
+  u32x4 resn;
   int g = 0;
   (void)tile_pass<STAGE, MODE>(args, smem, tl, c, cn, g, 0, w, wm, wn, lane, fo, res, resn, 0);
   MUON_WAIT_VMCNT(0);

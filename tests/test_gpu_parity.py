@@ -53,7 +53,7 @@ def test_flat_spectrum():
     take the same path through the iteration and any error in the polynomial's
     diagonal moves them all alike.  Stored in bf16 alone, B's diagonal left the
     512-row matrices at about 3e-2 (a CPU emulation of the rounding points);
-    with its rounding residual folded into the a*X term, about 9e-3."""
+    with the word per row that keeps it exact, about 9e-3."""
     say("[gpu] flat spectrum")
     shapes = [(512, 4096), (4096, 512), (256, 4096), (768, 768), (1024, 1024), (384, 1536)]
     steps = [[inputs.orthonormal_rows(r, c, 60 + i) for i, (r, c) in enumerate(shapes)]]
