@@ -51,6 +51,64 @@ def momentum_bytes(shapes, master: bool):
     return p * (2 + 4 + 4 + 2 + (1 if master else 0))
 
 
+def traffic_model(shapes, T, kmaster: int = 3, w_bytes: int = 4):
+    """Algorithmic HBM bytes of one step per kernel kind, bf16 products (every
+    short side >= 128), and of each update launch's iteration: what each kernel
+    must read and write once, with operand re-reads across tiles served from L2.
+
+    momentum: G (bf16) + M read and written + X0 (bf16 and, with kmaster > 0,
+    its low byte).  Per iteration t: Gram reads X (bf16) and writes A (m x m,
+    stored in full); the polynomial reads A and writes B; the update reads B and
+    X, X's low bytes when t <= kmaster, and writes the new X (and its low bytes
+    when t < kmaster), or, at t = T, reads and writes the fp32 weights instead.
+    B's diagonal words (4 m bytes per matrix) are left out."""
+    mom = gram = poly = 0
+    upd = [0] * T
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        mn, mm = m * n, m * m
+        mom += mn * (2 + 4 + 4 + 2 + (1 if kmaster > 0 else 0))
+        gram += mn * 2 + mm * 2
+        poly += mm * 2 + mm * 2
+        for t in range(1, T + 1):
+            b = mm * 2 + mn * 2 + (mn if t <= kmaster else 0)
+            b += 2 * mn * w_bytes if t == T else mn * 2 + (mn if t < kmaster else 0)
+            upd[t - 1] += b
+    return {"momentum": mom, "gram": T * gram, "poly": T * poly, "update": sum(upd), "update_per_iter": upd,
+            "gram_per_iter": gram, "poly_per_iter": poly}
+
+
+def step_floor_ms(work, traffic, T):
+    """The step's roofline floor: every launch at the larger of its MFMA time
+    (algorithmic FLOPs at the bf16 peak) and its HBM time (algorithmic bytes at
+    the HBM peak), summed over the step; momentum is HBM only.  The two matrix
+    groups split FLOPs and bytes alike, so whole-set sums per iteration serve."""
+    f = lambda flops, nbytes: max(flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9))
+    s = traffic["momentum"] / (PEAK_HBM_GBS * 1e9)
+    for t in range(T):
+        s += f(work["gram"], traffic["gram_per_iter"]) + f(work["poly"], traffic["poly_per_iter"])
+        s += f(work["update"], traffic["update_per_iter"][t])
+    return 1e3 * s
+
+
+def kernel_roofline(kind, flops, nbytes, ms):
+    """Roofline of one kernel from its algorithmic FLOPs and bytes per launch and
+    its average launch time: bound is the roof with the longer floor; the other
+    roof's view is kept beside it."""
+    t_f = flops / (PEAK_BF16_TFLOPS * 1e12) if flops else 0.0
+    t_b = nbytes / (PEAK_HBM_GBS * 1e9)
+    hbm = {"achieved": nbytes / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    hbm["frac"] = hbm["achieved"] / PEAK_HBM_GBS
+    if not flops:
+        return {"bound": "hbm", **hbm}
+    mfma = {"achieved": flops / (ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    mfma["frac"] = mfma["achieved"] / PEAK_BF16_TFLOPS
+    floors = {"mfma_us": 1e6 * t_f, "hbm_us": 1e6 * t_b}
+    if t_b > t_f:
+        return {"bound": "hbm", **hbm, "floors_per_launch": floors, "mfma_view": mfma}
+    return {"bound": "mfma", **mfma, "floors_per_launch": floors, "hbm_view": hbm}
+
+
 def read_profile_value(summary: str, key: str):
     """One value of a committed rocprofv3 counter summary (profiles/); None when
     there is none or the kernels changed since the counters were taken."""
@@ -125,7 +183,7 @@ def cpu_baseline(wl, reps: int = 3):
             "seconds_per_step": [round(t, 3) for t in times]}
 
 
-def after_timed_region(args, plan, grads, total, kw, wl, W, M, work, dom, fused):
+def after_timed_region(args, plan, grads, total, kw, wl, W, M, work, traffic, dom, fused):
     """Measurements after the timed region: the dominant kernel in a one-stream plan
     (staged plans), a per-iteration coefficient schedule, and the step replayed
     from a HIP graph."""
@@ -189,16 +247,11 @@ def after_timed_region(args, plan, grads, total, kw, wl, W, M, work, dom, fused)
     p1_ms, p1_cnt = plan1.read_profile()[dom]
     plan1.close()
     one_ms = p1_ms / p1_cnt
-    if dom == "momentum":
-        one_ach = momentum_bytes(wl.shapes, True) / (p1_cnt / one_steps) / (one_ms * 1e-3) / 1e9
-        one_peak = PEAK_HBM_GBS
-    else:
-        one_ach = wl.T * work[dom] / (p1_cnt / one_steps) / (one_ms * 1e-3) / 1e12
-        one_peak = PEAK_BF16_TFLOPS
-    roof_one = {"bound": "hbm" if dom == "momentum" else "mfma", "achieved": one_ach, "peak": one_peak,
-                "unit": "GB/s" if dom == "momentum" else "TFLOP/s",
-                "frac": one_ach / one_peak, "kernel": dom, "ms_per_launch": one_ms,
-                "note": f"one-stream plan (groups=1), {one_steps} steps after the timed region"}
+    per_step = p1_cnt / one_steps
+    flops = 0 if dom == "momentum" else wl.T * work[dom] / per_step
+    roof_one = kernel_roofline(dom, flops, traffic[dom] / per_step, one_ms)
+    roof_one.update({"kernel": dom, "ms_per_launch": one_ms,
+                     "note": f"one-stream plan (groups=1), {one_steps} steps after the timed region"})
 
     out["roofline_one_stream"] = roof_one
     return out
@@ -274,6 +327,7 @@ def main():
     torch.cuda.synchronize()
     prof_all = plan.read_profile()
     work = work_model(wl.shapes, wl.T)
+    traffic = traffic_model(wl.shapes, wl.T, 3 if args.x_master_iters < 0 else args.x_master_iters)
     per_kind = {}
     for k, (ms, cnt) in prof_all.items():
         if not cnt:
@@ -281,11 +335,12 @@ def main():
         per_kind[k] = {"ms_per_launch": ms / cnt, "launches_per_step": cnt / prof_steps}
         if k in ("gram", "poly", "update"):
             per_kind[k]["tflops"] = wl.T * work[k] / (cnt / prof_steps) / (ms / cnt * 1e-3) / 1e12
+            per_kind[k]["gbs"] = traffic[k] / (cnt / prof_steps) / (ms / cnt * 1e-3) / 1e9
         if k == "fused":
             per_kind[k]["tflops"] = work["step"] / (cnt / prof_steps) / (ms / cnt * 1e-3) / 1e12
     if "momentum" in per_kind:
         mk = per_kind["momentum"]
-        mk["gbs"] = momentum_bytes(wl.shapes, True) / mk["launches_per_step"] / (mk["ms_per_launch"] * 1e-3) / 1e9
+        mk["gbs"] = traffic["momentum"] / mk["launches_per_step"] / (mk["ms_per_launch"] * 1e-3) / 1e9
     dom = max(("gram", "poly", "update", "momentum", "fused"), key=lambda k: prof_all[k][0])
 
     # timed region: K steps, repeated.  HIP events taken by the library's own
@@ -318,7 +373,7 @@ def main():
 
     extras = {}
     if not args.no_extras:
-        extras = after_timed_region(args, plan, grads, total, kw, wl, W, M, work, dom, fused)
+        extras = after_timed_region(args, plan, grads, total, kw, wl, W, M, work, traffic, dom, fused)
     plan.close()
     ms_step = ms_total / args.steps
     steps_per_s = 1000.0 / ms_step
@@ -327,17 +382,12 @@ def main():
     d_launch_ms = d_ms / d_cnt
     d_per_step = d_cnt / prof_steps_timed
     if dom == "momentum":
-        achieved = momentum_bytes(wl.shapes, True) / d_per_step / (d_launch_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS}
+        roof = kernel_roofline(dom, 0, traffic["momentum"] / d_per_step, d_launch_ms)
     elif dom == "fused":
-        achieved = work["step"] / d_per_step / (d_launch_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS}
+        nb = traffic["gram"] + traffic["poly"] + traffic["update"]
+        roof = kernel_roofline(dom, work["step"] / d_per_step, nb / d_per_step, d_launch_ms)
     else:
-        achieved = wl.T * work[dom] / d_per_step / (d_launch_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS}
+        roof = kernel_roofline(dom, wl.T * work[dom] / d_per_step, traffic[dom] / d_per_step, d_launch_ms)
     roof["kernel"] = dom
     roof["scope"] = (f"per launch of the dominant kernel, averaged over its launches in {prof_steps_timed} steps "
                      f"of the timed region (one step in {prof_every})")
@@ -347,15 +397,21 @@ def main():
     # share of SIMD cycles with the MFMA unit busy (rocprofv3 counters), when fresh
     roof["mfma_busy"] = read_profile_value("mfma_busy", f"{dom}_mfma_busy")
     roof["step_frac"] = tflops / PEAK_BF16_TFLOPS
+    floor_ms = step_floor_ms(work, traffic, wl.T)
+    roof["step_roofline"] = {"floor_ms": floor_ms, "measured_ms": ms_step, "frac": floor_ms / ms_step,
+                             "note": "sum over the step's launches of the longer of each launch's MFMA and HBM "
+                                     "floors (algorithmic FLOPs and bytes at the peaks), over the measured step"}
     if fused:
         roof["note"] = ("the fused launch runs every Newton-Schulz product of the step (all T iterations) on one "
                         "stream; frac is its algorithmic rate over its own duration, step_frac the whole step's "
                         "(momentum and norm included) against the same peak")
     else:
-        roof["note"] = ("frac is per launch: the plan runs two matrix groups on two streams, so each launch covers "
-                        "half the set and shares the GPU with the other group's launches; step_frac is the whole "
-                        "step's algorithmic rate against the same peak, and roofline_one_stream the kernel's own "
-                        "rate without the overlap")
+        roof["note"] = ("frac is per launch, against the roof whose floor is longer for the kernel's algorithmic "
+                        "FLOPs and bytes (floors_per_launch); the plan runs two matrix groups on two streams, so "
+                        "each launch covers half the set and shares the GPU with the other group's launches; "
+                        "step_frac is the whole step's algorithmic FLOP rate against the bf16 peak, step_roofline "
+                        "the step against the sum of its launches' floors, and roofline_one_stream the kernel's "
+                        "own rate without the overlap")
 
     out = {
         "metric": "Muon steps/s on GPT-2-small hidden set (T=5); % bf16 MFMA peak",
