@@ -85,21 +85,26 @@ struct Shape {
   static_assert(4 * kBlock <= kSlot, "staged epilogue blocks fit one slot");
 };
 
-// Swizzles (16-byte chunk c of row r sits at chunk c ^ swz(r)), each checked
-// in a bank model of 16 lanes per 256-byte cycle for its access patterns.
+// Swizzles (16-byte chunk c of row r sits at chunk c ^ swz(r)).  Bank model,
+// from rocprofv3 bank-conflict counts of each access pattern on gfx950:
+// 16-byte reads serve 16 lanes per clock over 256 bytes, 8-byte reads 32
+// lanes over 256 bytes, 4-byte reads 32 lanes over 128 bytes, and 16-byte
+// writes 8 lanes over 128 bytes.
 // K-contiguous half slab (64-byte rows): MFMA fragment reads (32 rows x one
 // chunk per 32 lanes) conflict-free.
 __device__ __forceinline__ int kc_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 // X slab of B X (32 K rows x 128 columns, four 32-column tiles; in LDS as
 // [tile][32 rows][64 bytes]): transposing fragment reads (4 K rows x 2 chunks
-// per 16 lanes) and row reads of the a X term (16 rows x one chunk)
-// conflict-free.
+// per 16 lanes) conflict-free; the a X term's 8-byte row reads 2-way.
 __device__ __forceinline__ int xs_swz(int k) { return (k >> 2) & 3; }
 // Low bytes of that slab ([tile][32 rows][32 bytes], 16-byte halves of row k
-// at half ^ lo_swz(k)): row reads conflict-free.
+// at half ^ lo_swz(k)): the a X term's 4-byte row reads 4-way.  Those two
+// conflicts cost nothing measurable (16-byte reads without them: same step).
 __device__ __forceinline__ int lo_swz(int k) { return (k >> 3) & 1; }
-// Staged 32 x 32 fp32 block (128-byte rows): accumulator writes and row passes
-// conflict-free, 4 x 4 block reads 2-way.
+// Staged 32 x 32 fp32 block (128-byte rows): row-pass reads conflict-free,
+// accumulator writes, row-pass writes and 4 x 4 block reads 2-way.  A
+// swizzle that made the writes conflict-free, r ^ ((r >> 1) & 1), cost
+// registers and no time.
 __device__ __forceinline__ int st_swz(int r) { return (r >> 1) & 7; }
 
 // Two of the eight 1 KiB instructions that fill a K-contiguous half slab
