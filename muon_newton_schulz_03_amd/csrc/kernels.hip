@@ -542,19 +542,25 @@ constexpr int kStageLds = 2 * kSlabLds;
 constexpr int kBlocksPerCu = 2;
 
 
-// One block per matrix: s = 1 / (||U||_F + eps) from the momentum kernel's
-// per-tile partial sums (fixed summation order: deterministic).
-__global__ __launch_bounds__(kThreads) void norm_kernel(const DevMat* mats) {
+// One wave per matrix: s = 1 / (||U||_F + eps) from the momentum kernel's
+// per-tile partial sums, lane-strided fp64 sums and a fixed butterfly
+// (deterministic).  It uses no LDS, so it starts beside the other matrix
+// group's persistent product blocks, which hold every CU's LDS; with a
+// shared-memory tree it waited tens of microseconds for a slot.
+__global__ __launch_bounds__(64) void norm_kernel(const DevMat* mats) {
   const DevMat d = mats[blockIdx.x];
-  __shared__ double scratch[kThreads];
-  double nu;
-  const float inv = block_inv_norm(d, scratch, &nu);
-  if (threadIdx.x == 0) {
-    gv<float>(d.sc)[0] = inv;
+  const int lane = threadIdx.x;
+  double s = 0.0;
+  for (int p = lane; p < d.nparts; p += 64) s += (double)gv<float>(d.part)[p];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+  if (lane == 0) {
+    const double nu = sqrt(s);
+    gv<float>(d.sc)[0] = (float)(1.0 / (nu + kEps));
     gv<float>(d.sc)[1] = (float)nu;
     if (d.dep) *gv<int32_t>(d.dep) = 0;  // the fused launch's counters start each step at zero
   }
-  if (d.heads && threadIdx.x < kXcds) gv<int32_t>(d.heads)[threadIdx.x] = 0;
+  if (d.heads && lane < kXcds) gv<int32_t>(d.heads)[lane] = 0;
 }
 
 // Where a tile's operand panels are, and its K extent (wave-uniform).  A
@@ -1049,7 +1055,8 @@ __host__ hipError_t launch(const void* fn, int blocks, size_t lds, const A& args
 }
 
 hipError_t launch_norm(const DevMat* mats, int n, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  return launch((const void*)norm_kernel, n, 0, mats, stream, ev0, ev1);
+  void* kargs[] = {(void*)&mats};
+  return hipExtLaunchKernel((const void*)norm_kernel, dim3(n), dim3(64), kargs, 0, stream, ev0, ev1, 0);
 }
 
 #define MUON_STAGE_KERNEL(S, F, M) ((const void*)ns_stage_kernel<S, F, M>)
